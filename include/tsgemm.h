@@ -1,0 +1,135 @@
+/*
+ * tsgemm.h -- C ABI of the persistent, tile-scheduled dense GEMM for MI355X
+ * (gfx950 / CDNA4).  Library: libtsgemm.so.
+ *
+ *   C[M,N] = A[M,K] * B[K,N]
+ *
+ * A, B and C are row-major and contiguous and share one 16-bit dtype (fp16 or
+ * bf16); products accumulate in fp32 and each C element is rounded once to the
+ * dtype (round to nearest, ties to even).  This is the product computed by the
+ * persistent example of page "[Feature] Introduce tile scheduler #2441" (diff of
+ * examples/gemm_sm100/gemm_tcgen5mma_ws_persistent.py: A[M,K] and B[K,N]
+ * copied slab by slab into shared memory, accumulated into an fp32 tile, cast
+ * and stored; checked against torch `a @ b` in main()).
+ *
+ * A fixed grid of persistent workgroups runs one loop each, driven by a tile
+ * scheduler that owns the wave clock w: worker `wid` visits
+ * tile_id = P*w + wid while tile_id < num_tiles, decoding it into (m_idx, n_idx)
+ * in groups of `group_size` column blocks (same page: the manual tile walk that
+ * PersistentTileScheduler(..., swizzle_size=group_size) replaces; the page's
+ * conversation tab lists init / valid / next_tile and coord(tile_id)).  When
+ * n_blocks is not a multiple of group_size the last group is narrower.
+ *
+ * Conventions (the page "tilelang" blog, section 1.3, shows the host stubs this
+ * follows: init / call(A, B, C, stream) returning 0 or -1 with the message in
+ * get_last_error(), and the argument checks of the lowered host function):
+ *   - every int-returning call returns TSGEMM_OK (0) or a negative TSGEMM_E*
+ *     code and then sets a message readable with tsgemm_last_error();
+ *   - pointer arguments named A, B, C are DEVICE pointers, the caller owns
+ *     them; `out` arguments of the schedule calls are HOST pointers;
+ *   - the library keeps no pointer after a call returns; a plan is immutable
+ *     once configured (create + the set_* calls), so concurrent runs of one
+ *     plan on different streams are safe.
+ */
+#ifndef TSGEMM_H
+#define TSGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tsgemm_plan tsgemm_plan; /* opaque, owned by the library */
+
+enum { TSGEMM_FP16 = 1, TSGEMM_BF16 = 2 };
+
+enum {
+    TSGEMM_OK = 0,
+    TSGEMM_EINVAL = -1,       /* malformed argument                              */
+    TSGEMM_EUNSUPPORTED = -2, /* well-formed but outside the compiled kernels    */
+    TSGEMM_EHIP = -3,         /* a HIP runtime call failed (no device, launch)   */
+    TSGEMM_ENOMEM = -4        /* allocation failed                               */
+};
+
+/* Plan summary; every field is derived at create/configure time. */
+typedef struct tsgemm_info {
+    int64_t M, N, K;
+    int32_t dtype;
+    int32_t block_M, block_N, block_K;
+    int32_t group_size;
+    int32_t num_stages;      /* as requested                                         */
+    int32_t lds_slots;       /* K-slabs resident in LDS: min(num_stages, LDS / stage) */
+    int32_t stage_bytes;     /* (block_M*block_K + block_K*block_N) * 2              */
+    int32_t lds_bytes;       /* lds_slots * stage_bytes                              */
+    int64_t m_blocks, n_blocks, k_blocks, num_tiles;
+    int32_t num_workgroups;  /* P; 0 while unresolved (default P before a device is seen) */
+    int32_t waves;           /* ceil(num_tiles / P); 0 while P is unresolved         */
+    int32_t threads_per_workgroup;
+    int32_t xcd_remap;       /* 1: workgroup -> worker id permuted so XCDs get compact tile blocks */
+} tsgemm_info;
+
+/*
+ * Validate a problem and build a plan.  Returns NULL on error (message in
+ * tsgemm_last_error()).  Makes no HIP call.
+ *   M, N, K      >= 0; K % block_K == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows,
+ *                as the lowered host function's "divisible by 8" check);
+ *                block_M*K*2, block_K*N*2 and block_M*N*2 below 2^31 (per-tile
+ *                32-bit offsets); M, N < 2^31.
+ *   dtype        TSGEMM_FP16 or TSGEMM_BF16 (A, B and C).
+ *   block_M/N/K  one of 128x128x32, 128x128x64, 256x256x32, 256x256x64.
+ *   group_size   >= 1, column blocks per rasterisation group.
+ *   num_stages   >= 2: K-slabs in flight; the LDS ring holds
+ *                min(num_stages, floor(160 KiB / stage_bytes)) of them.
+ * The number of workgroups defaults to one per compute unit of the device
+ * current at the first run (see tsgemm_set_num_workgroups).
+ */
+tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype,
+                           int block_M, int block_N, int block_K,
+                           int group_size, int num_stages);
+
+/* Fix the persistent grid size P (>= 1); 0 restores "one per compute unit". */
+int tsgemm_set_num_workgroups(tsgemm_plan* plan, int num_workgroups);
+
+/* Enable (1, default) or disable (0) the XCD-aware workgroup -> worker id
+ * permutation.  The schedule is defined on worker ids either way. */
+int tsgemm_set_xcd_remap(tsgemm_plan* plan, int enable);
+
+/* Asynchronously compute C = A*B on `stream` (a hipStream_t; NULL = default
+ * stream).  A, B, C: device pointers, 16-byte aligned, holding M*K, K*N and
+ * M*N elements; C is fully overwritten and must not overlap A or B.  Buffers
+ * must stay alive until the stream work completes.  M*N == 0 launches nothing. */
+int tsgemm_run(const tsgemm_plan* plan, const void* A, const void* B, void* C, void* stream);
+
+/* Same as tsgemm_run and additionally records every tile the GEMM kernel
+ * processes: trace (DEVICE pointer, int32[4 * P * max_iters], max_iters =
+ * ceil(num_tiles / P)) receives (worker, iter, m_idx, n_idx) at row
+ * worker*max_iters + iter.  Diagnostic; rows not visited are left untouched. */
+int tsgemm_run_traced(const tsgemm_plan* plan, const void* A, const void* B, void* C,
+                      void* stream, int32_t* trace);
+
+int64_t tsgemm_num_tiles(const tsgemm_plan* plan);       /* < 0 on error                */
+int tsgemm_num_workgroups(const tsgemm_plan* plan);      /* resolves the default P      */
+int tsgemm_plan_info(const tsgemm_plan* plan, tsgemm_info* info);
+
+/* Run the scheduler on the device over the plan's persistent grid and write
+ * num_tiles rows of int32 (worker, iter, m_idx, n_idx), sorted by
+ * (worker, iter), to the HOST buffer `out` (4 * num_tiles int32).
+ * Synchronous (default stream). */
+int tsgemm_dump_schedule(const tsgemm_plan* plan, int32_t* out);
+
+/* The same rows computed on the host by the same scheduler code compiled for
+ * the CPU, for `num_workgroups` workers (> 0).  Makes no HIP call. */
+int tsgemm_schedule_host(const tsgemm_plan* plan, int num_workgroups, int32_t* out);
+
+void tsgemm_destroy(tsgemm_plan* plan);                  /* NULL-safe */
+
+/* Message of the last failing call on this thread ("" if none).  Valid until
+ * the next tsgemm call on the same thread. */
+const char* tsgemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSGEMM_H */

@@ -1,0 +1,204 @@
+"""Python binding of libtsgemm (include/tsgemm.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels; PyTorch only provides
+device memory and the stream.  Importing works without a GPU (plan creation and
+validation are host-only); running needs the built library and a gfx950 GPU,
+and fails loudly otherwise.
+
+Names follow the C ABI: ``create`` -> :class:`Plan`, ``Plan.run``,
+``Plan.run_traced``, ``Plan.dump_schedule``, ``Plan.schedule_host``,
+``Plan.info``, ``last_error``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtsgemm.so")
+
+FP16 = 1
+BF16 = 2
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, -1, -2, -3, -4
+
+# every symbol the header declares
+EXPORTS = (
+    "tsgemm_create", "tsgemm_set_num_workgroups", "tsgemm_set_xcd_remap", "tsgemm_run",
+    "tsgemm_run_traced", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
+    "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
+)
+
+
+class TsgemmError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"tsgemm error {code}: {msg}")
+        self.code = code
+
+
+class Info(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("block_M", ctypes.c_int32), ("block_N", ctypes.c_int32), ("block_K", ctypes.c_int32),
+        ("group_size", ctypes.c_int32), ("num_stages", ctypes.c_int32),
+        ("lds_slots", ctypes.c_int32), ("stage_bytes", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+        ("m_blocks", ctypes.c_int64), ("n_blocks", ctypes.c_int64), ("k_blocks", ctypes.c_int64),
+        ("num_tiles", ctypes.c_int64),
+        ("num_workgroups", ctypes.c_int32), ("waves", ctypes.c_int32),
+        ("threads_per_workgroup", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libtsgemm.so (built by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
+                           "(persistent_tile_scheduled_amd._build.build_library())")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.tsgemm_create.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32]
+    lib.tsgemm_create.restype = vp
+    lib.tsgemm_set_num_workgroups.argtypes = [vp, i32]
+    lib.tsgemm_set_num_workgroups.restype = i32
+    lib.tsgemm_set_xcd_remap.argtypes = [vp, i32]
+    lib.tsgemm_set_xcd_remap.restype = i32
+    lib.tsgemm_run.argtypes = [vp, vp, vp, vp, vp]
+    lib.tsgemm_run.restype = i32
+    lib.tsgemm_run_traced.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.tsgemm_run_traced.restype = i32
+    lib.tsgemm_num_tiles.argtypes = [vp]
+    lib.tsgemm_num_tiles.restype = i64
+    lib.tsgemm_num_workgroups.argtypes = [vp]
+    lib.tsgemm_num_workgroups.restype = i32
+    lib.tsgemm_plan_info.argtypes = [vp, ctypes.POINTER(Info)]
+    lib.tsgemm_plan_info.restype = i32
+    lib.tsgemm_dump_schedule.argtypes = [vp, i32p]
+    lib.tsgemm_dump_schedule.restype = i32
+    lib.tsgemm_schedule_host.argtypes = [vp, i32, i32p]
+    lib.tsgemm_schedule_host.restype = i32
+    lib.tsgemm_destroy.argtypes = [vp]
+    lib.tsgemm_destroy.restype = None
+    lib.tsgemm_last_error.argtypes = []
+    lib.tsgemm_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().tsgemm_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise TsgemmError(rc, last_error())
+    return rc
+
+
+_DTYPES = {"fp16": FP16, "bf16": BF16, FP16: FP16, BF16: BF16}
+
+
+class Plan:
+    """A validated problem (tsgemm_create).  Immutable once configured."""
+
+    def __init__(self, M: int, N: int, K: int, dtype, block_M: int, block_N: int, block_K: int,
+                 group_size: int, num_stages: int, num_workgroups: int = 0, xcd_remap: bool = True):
+        lib = load()
+        self._lib = lib
+        dt = _DTYPES.get(dtype)
+        if dt is None:
+            import torch
+            dt = {torch.float16: FP16, torch.bfloat16: BF16}.get(dtype, 0)
+        h = lib.tsgemm_create(M, N, K, dt, block_M, block_N, block_K, group_size, num_stages)
+        if not h:
+            msg = last_error()
+            raise TsgemmError(EUNSUPPORTED if "compiled" in msg or "fit" in msg or "exceeds" in msg
+                              else EINVAL, msg)
+        self._h = ctypes.c_void_p(h)
+        self.M, self.N, self.K, self.dtype = M, N, K, dt
+        if num_workgroups:
+            _check(lib.tsgemm_set_num_workgroups(self._h, num_workgroups))
+        _check(lib.tsgemm_set_xcd_remap(self._h, 1 if xcd_remap else 0))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.tsgemm_destroy(h)
+            self._h = None
+
+    # -- queries -------------------------------------------------------------
+    @property
+    def num_tiles(self) -> int:
+        return _check(self._lib.tsgemm_num_tiles(self._h))
+
+    @property
+    def num_workgroups(self) -> int:
+        return _check(self._lib.tsgemm_num_workgroups(self._h))
+
+    def info(self) -> dict:
+        inf = Info()
+        _check(self._lib.tsgemm_plan_info(self._h, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    # -- schedule ------------------------------------------------------------
+    def schedule_host(self, num_workgroups: int) -> np.ndarray:
+        out = np.empty((self.num_tiles, 4), dtype=np.int32)
+        _check(self._lib.tsgemm_schedule_host(self._h, num_workgroups,
+                                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return out
+
+    def dump_schedule(self) -> np.ndarray:
+        out = np.empty((self.num_tiles, 4), dtype=np.int32)
+        _check(self._lib.tsgemm_dump_schedule(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return out
+
+    # -- run -----------------------------------------------------------------
+    def _args(self, A, B, C):
+        import torch
+        want = torch.float16 if self.dtype == FP16 else torch.bfloat16
+        for name, t, shape in (("A", A, (self.M, self.K)), ("B", B, (self.K, self.N)), ("C", C, (self.M, self.N))):
+            if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous {want} CUDA tensor of shape {shape}")
+        return A.data_ptr(), B.data_ptr(), C.data_ptr()
+
+    def run(self, A, B, C, stream=None) -> None:
+        """C = A @ B on `stream` (a torch.cuda.Stream; default: torch's current stream)."""
+        import torch
+        a, b, c = self._args(A, B, C)
+        s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        _check(self._lib.tsgemm_run(self._h, a, b, c, s))
+
+    def run_traced(self, A, B, C, trace, stream=None) -> None:
+        import torch
+        a, b, c = self._args(A, B, C)
+        if trace.dtype != torch.int32 or not trace.is_cuda or not trace.is_contiguous():
+            raise ValueError("trace must be a contiguous int32 CUDA tensor")
+        s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        _check(self._lib.tsgemm_run_traced(self._h, a, b, c, s, trace.data_ptr()))
+
+
+def matmul(A, B, block_M=256, block_N=256, block_K=64, group_size=8, num_stages=3):
+    """Convenience: C = A @ B with a fresh plan (allocates C with torch)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    plan = Plan(M, N, K, A.dtype, block_M, block_N, block_K, group_size, num_stages)
+    C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    plan.run(A, B, C)
+    return C

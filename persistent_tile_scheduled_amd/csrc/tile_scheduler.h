@@ -1,0 +1,88 @@
+// Persistent tile scheduler, compiled both for the host and for gfx950.
+//
+// Page "[Feature] Introduce tile scheduler #2441" (diff of
+// examples/gemm_sm100/gemm_tcgen5mma_ws_persistent.py): each warp role builds
+// its own PersistentTileScheduler, calls init(block_id), loops while valid()
+// and advances with next_tile(); the scheduler's current_iter is the wave index
+// w (pipeline phase, w & 1 double buffering) and m_idx / n_idx are the tile
+// coordinates.  The removed manual walk it replaces gives worker `wid` the
+// linear tiles P*w + wid and decodes them in groups of group_size column
+// blocks, rows of the group walked one after the other.  The conversation tab
+// describes a stateless coord(tile_id) next to the stateful iteration.
+//
+// Here every wavefront keeps its own copy in scalar registers (all members are
+// wave-uniform), the loader and the MMA loop each hold one, as the page's
+// roles do, and no coordinates are exchanged between them.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TSG_HD __host__ __device__ __forceinline__
+#else
+#define TSG_HD inline
+#endif
+
+namespace tsg {
+
+struct TileScheduler {
+    uint32_t num_workers;  // P
+    uint32_t m_blocks, n_blocks, group, tiles;
+    uint32_t worker, iter, tile_id;
+    uint32_t m_idx, n_idx;
+
+    TSG_HD void setup(uint32_t P, uint32_t mb, uint32_t nb, uint32_t gs) {
+        num_workers = P;
+        m_blocks = mb;
+        n_blocks = nb;
+        group = gs;
+        tiles = mb * nb;
+    }
+
+    // Decode one linear tile id: column group g covers n blocks
+    // [g*group, g*group + width), width = group except a narrower last group;
+    // inside the group tiles run row by row.
+    TSG_HD void coord(uint32_t t, uint32_t& m, uint32_t& n) const {
+        const uint32_t per_group = group * m_blocks;
+        const uint32_t g = t / per_group;
+        const uint32_t first = g * group;
+        const uint32_t rest = n_blocks - first;
+        const uint32_t width = rest < group ? rest : group;
+        const uint32_t r = t - g * per_group;
+        const uint32_t row = r / width;
+        m = row;
+        n = first + (r - row * width);
+    }
+
+    TSG_HD void init(uint32_t wid) {
+        worker = wid;
+        iter = 0;
+        tile_id = wid;
+        update();
+    }
+    TSG_HD bool valid() const { return tile_id < tiles; }
+    TSG_HD void next_tile() {
+        ++iter;
+        tile_id += num_workers;
+        update();
+    }
+    TSG_HD uint32_t parity() const { return iter & 1u; }
+
+  private:
+    TSG_HD void update() {
+        if (valid()) coord(tile_id, m_idx, n_idx);
+    }
+};
+
+// Hardware hands workgroups to the XCDs round robin (workgroup b runs on XCD
+// b % X).  Renumber them so that XCD x holds a contiguous run of worker ids:
+// consecutive tile ids, hence a compact block of one column group, then share
+// that XCD's L2.  A bijection on [0, P) for every P.
+TSG_HD uint32_t worker_of_workgroup(uint32_t b, uint32_t P, uint32_t X) {
+    if (X <= 1u) return b;
+    const uint32_t x = b % X, j = b / X;
+    const uint32_t q = P / X, r = P % X;
+    return x * q + (x < r ? x : r) + j;
+}
+
+}  // namespace tsg

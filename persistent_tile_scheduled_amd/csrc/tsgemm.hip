@@ -1,0 +1,329 @@
+// libtsgemm: C ABI around the persistent tile-scheduled GEMM kernels
+// (declarations and contracts: include/tsgemm.h).
+//
+// Host conventions follow the lowered host code on page "tilelang" (blog,
+// section 1.3): argument checks before any launch, 0 / negative return codes,
+// and the failure message kept for a get_last_error() call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "tsgemm.h"
+#include "tile_scheduler.h"
+#include "tsgemm_kernel.h"
+
+namespace {
+
+constexpr int kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
+constexpr int kMaxSlots = 4;           // deepest compiled LDS ring
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+typedef void (*launch_fn)(const tsg::GemmArgs&, unsigned grid, hipStream_t);
+
+template <int DT, int BM, int BN, int BK, int L>
+void launch(const tsg::GemmArgs& a, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((tsg::tsgemm_kernel<DT, BM, BN, BK, L>), dim3(grid), dim3(tsg::kThreads), 0, s, a);
+}
+
+struct KernelEntry {
+    int dt, bm, bn, bk, slots;
+    launch_fn fn;
+};
+
+#define TSG_TILE(DT, BM, BN, BK)                                            \
+    {DT, BM, BN, BK, 2, launch<DT, BM, BN, BK, 2>},                         \
+    {DT, BM, BN, BK, 3, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 3 <= kLdsBytes) ? 3 : 2>}, \
+    {DT, BM, BN, BK, 4, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 4 <= kLdsBytes) ? 4 : 2>}
+
+const KernelEntry kKernels[] = {
+    TSG_TILE(1, 128, 128, 32), TSG_TILE(1, 128, 128, 64), TSG_TILE(1, 256, 256, 32), TSG_TILE(1, 256, 256, 64),
+    TSG_TILE(2, 128, 128, 32), TSG_TILE(2, 128, 128, 64), TSG_TILE(2, 256, 256, 32), TSG_TILE(2, 256, 256, 64),
+};
+
+const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots) {
+    for (const KernelEntry& e : kKernels)
+        if (e.dt == dt && e.bm == bm && e.bn == bn && e.bk == bk && e.slots == slots) return &e;
+    return nullptr;
+}
+
+bool tile_supported(int bm, int bn, int bk) {
+    return (bm == 128 && bn == 128 && (bk == 32 || bk == 64)) ||
+           (bm == 256 && bn == 256 && (bk == 32 || bk == 64));
+}
+
+// Persistent grid default: one workgroup per compute unit of the device.
+std::atomic<int> g_cu_count[64];
+
+int device_cus(int* cus, int* xcds) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TSGEMM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    int n = (dev >= 0 && dev < 64) ? g_cu_count[dev].load() : 0;
+    if (n <= 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || n <= 0)
+            return fail(TSGEMM_EHIP, "cannot query the compute-unit count: %s", hipGetErrorString(e));
+        if (dev >= 0 && dev < 64) g_cu_count[dev].store(n);
+    }
+    *cus = n;
+    // MI300-class parts expose 8 XCDs per device in single-partition mode.
+    *xcds = n >= 128 ? 8 : 1;
+    return TSGEMM_OK;
+}
+
+}  // namespace
+
+struct tsgemm_plan {
+    int64_t M, N, K;
+    int dtype, bm, bn, bk, group, stages, slots;
+    int64_t m_blocks, n_blocks, k_blocks, tiles;
+    int P;         // 0 = default (compute units)
+    int xcd_remap; // 1 = permute workgroups so each XCD runs consecutive worker ids
+    const KernelEntry* kernel;
+};
+
+namespace {
+
+struct Grid {
+    uint32_t P, xcds, max_iters;
+};
+
+int resolve_grid(const tsgemm_plan* p, Grid* g) {
+    int cus = 0, xcds = 1;
+    if (p->P == 0 || p->xcd_remap) {
+        int rc = device_cus(&cus, &xcds);
+        if (rc != TSGEMM_OK) return rc;
+    }
+    g->P = (uint32_t)(p->P ? p->P : cus);
+    g->xcds = p->xcd_remap ? (uint32_t)xcds : 1u;
+    g->max_iters = (uint32_t)((p->tiles + g->P - 1) / g->P);
+    return TSGEMM_OK;
+}
+
+int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* stream, int32_t* trace) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (p->M == 0 || p->N == 0) return TSGEMM_OK;  // empty output: nothing to launch
+    if (!C) return fail(TSGEMM_EINVAL, "C is NULL");
+    if (p->K > 0 && (!A || !B)) return fail(TSGEMM_EINVAL, "A or B is NULL");
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) | reinterpret_cast<uintptr_t>(C)) & 15u)
+        return fail(TSGEMM_EINVAL, "A, B and C must be 16-byte aligned");
+    Grid g;
+    int rc = resolve_grid(p, &g);
+    if (rc != TSGEMM_OK) return rc;
+    tsg::GemmArgs a;
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = static_cast<uint16_t*>(C);
+    a.trace = trace;
+    a.M = p->M;
+    a.N = p->N;
+    a.K = p->K;
+    a.m_blocks = (uint32_t)p->m_blocks;
+    a.n_blocks = (uint32_t)p->n_blocks;
+    a.k_blocks = (uint32_t)p->k_blocks;
+    a.group = (uint32_t)p->group;
+    a.P = g.P;
+    a.max_iters = g.max_iters;
+    a.num_xcd = g.xcds;
+    (void)hipGetLastError();
+    if (p->k_blocks == 0) {
+        // empty sum: C = 0 (N % 8 == 0, so 8 elements per thread)
+        const int64_t count8 = p->M * p->N / 8;
+        const unsigned blocks = (unsigned)((count8 + 255) / 256);
+        hipLaunchKernelGGL(tsg::tsgemm_zero_kernel, dim3(blocks), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), a.C, count8);
+    } else {
+        p->kernel->fn(a, g.P, static_cast<hipStream_t>(stream));
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TSGEMM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return TSGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tsgemm_last_error(void) { return g_err; }
+
+tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block_M, int block_N,
+                           int block_K, int group_size, int num_stages) {
+    g_err[0] = '\0';
+    if (M < 0 || N < 0 || K < 0) { fail(TSGEMM_EINVAL, "M, N, K must be >= 0"); return nullptr; }
+    if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) {
+        fail(TSGEMM_EINVAL, "M, N and K must be below 2^31"); return nullptr;
+    }
+    if (dtype != TSGEMM_FP16 && dtype != TSGEMM_BF16) {
+        fail(TSGEMM_EINVAL, "dtype must be TSGEMM_FP16 (1) or TSGEMM_BF16 (2), got %d", dtype); return nullptr;
+    }
+    if (block_M <= 0 || block_N <= 0 || block_K <= 0) { fail(TSGEMM_EINVAL, "block sizes must be positive"); return nullptr; }
+    if (group_size < 1) { fail(TSGEMM_EINVAL, "group_size must be >= 1, got %d", group_size); return nullptr; }
+    if (num_stages < 2) { fail(TSGEMM_EINVAL, "num_stages must be >= 2, got %d", num_stages); return nullptr; }
+    if (K % block_K != 0) {
+        fail(TSGEMM_EINVAL, "K (%lld) must be a multiple of block_K (%d)", (long long)K, block_K); return nullptr;
+    }
+    if (N % 8 != 0 || K % 8 != 0) {
+        fail(TSGEMM_EINVAL, "N and K must be divisible by 8 (16-byte rows)"); return nullptr;
+    }
+    if (!tile_supported(block_M, block_N, block_K)) {
+        fail(TSGEMM_EUNSUPPORTED, "tile %dx%dx%d is not compiled (have 128x128x{32,64}, 256x256x{32,64})",
+             block_M, block_N, block_K);
+        return nullptr;
+    }
+    const int64_t lim = int64_t(1) << 31;
+    if (int64_t(block_M) * K * 2 >= lim || int64_t(block_K) * N * 2 >= lim || int64_t(block_M) * N * 2 >= lim) {
+        fail(TSGEMM_EUNSUPPORTED, "a tile's byte extent (block_M*K*2, block_K*N*2, block_M*N*2) exceeds 2^31");
+        return nullptr;
+    }
+    const int stage = (block_M * block_K + block_K * block_N) * 2;
+    int slots = kLdsBytes / stage;
+    if (slots > num_stages) slots = num_stages;
+    if (slots > kMaxSlots) slots = kMaxSlots;
+    if (slots < 2) { fail(TSGEMM_EUNSUPPORTED, "two %d-byte stages do not fit in LDS", stage); return nullptr; }
+    const int64_t mb = (M + block_M - 1) / block_M, nb = (N + block_N - 1) / block_N;
+    if (mb * nb >= lim) { fail(TSGEMM_EUNSUPPORTED, "tile count must be below 2^31"); return nullptr; }
+    const KernelEntry* k = find_kernel(dtype, block_M, block_N, block_K, slots);
+    if (!k) { fail(TSGEMM_EUNSUPPORTED, "no kernel for this configuration"); return nullptr; }
+    tsgemm_plan* p = new (std::nothrow) tsgemm_plan;
+    if (!p) { fail(TSGEMM_ENOMEM, "out of host memory"); return nullptr; }
+    p->M = M; p->N = N; p->K = K;
+    p->dtype = dtype; p->bm = block_M; p->bn = block_N; p->bk = block_K;
+    p->group = group_size; p->stages = num_stages; p->slots = slots;
+    p->m_blocks = mb; p->n_blocks = nb; p->k_blocks = K / block_K; p->tiles = mb * nb;
+    p->P = 0; p->xcd_remap = 1; p->kernel = k;
+    return p;
+}
+
+int tsgemm_set_num_workgroups(tsgemm_plan* p, int num_workgroups) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (num_workgroups < 0) return fail(TSGEMM_EINVAL, "num_workgroups must be >= 0");
+    p->P = num_workgroups;
+    return TSGEMM_OK;
+}
+
+int tsgemm_set_xcd_remap(tsgemm_plan* p, int enable) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (enable != 0 && enable != 1) return fail(TSGEMM_EINVAL, "enable must be 0 or 1");
+    p->xcd_remap = enable;
+    return TSGEMM_OK;
+}
+
+int tsgemm_run(const tsgemm_plan* p, const void* A, const void* B, void* C, void* stream) {
+    return run_impl(p, A, B, C, stream, nullptr);
+}
+
+int tsgemm_run_traced(const tsgemm_plan* p, const void* A, const void* B, void* C, void* stream,
+                      int32_t* trace) {
+    if (!trace) return fail(TSGEMM_EINVAL, "trace is NULL");
+    return run_impl(p, A, B, C, stream, trace);
+}
+
+int64_t tsgemm_num_tiles(const tsgemm_plan* p) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    return p->tiles;
+}
+
+int tsgemm_num_workgroups(const tsgemm_plan* p) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (p->P) return p->P;
+    int cus = 0, xcds = 1;
+    int rc = device_cus(&cus, &xcds);
+    return rc != TSGEMM_OK ? rc : cus;
+}
+
+int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
+    g_err[0] = '\0';
+    if (!p || !info) return fail(TSGEMM_EINVAL, "plan or info is NULL");
+    std::memset(info, 0, sizeof(*info));
+    info->M = p->M; info->N = p->N; info->K = p->K;
+    info->dtype = p->dtype;
+    info->block_M = p->bm; info->block_N = p->bn; info->block_K = p->bk;
+    info->group_size = p->group;
+    info->num_stages = p->stages;
+    info->lds_slots = p->slots;
+    info->stage_bytes = (p->bm * p->bk + p->bk * p->bn) * 2;
+    info->lds_bytes = info->stage_bytes * p->slots;
+    info->m_blocks = p->m_blocks; info->n_blocks = p->n_blocks;
+    info->k_blocks = p->k_blocks; info->num_tiles = p->tiles;
+    info->num_workgroups = p->P;  // explicit P only; default resolves at run time
+    info->waves = p->P ? (int32_t)((p->tiles + p->P - 1) / p->P) : 0;
+    info->threads_per_workgroup = tsg::kThreads;
+    info->xcd_remap = p->xcd_remap;
+    return TSGEMM_OK;
+}
+
+int tsgemm_schedule_host(const tsgemm_plan* p, int num_workgroups, int32_t* out) {
+    g_err[0] = '\0';
+    if (!p || !out) return fail(TSGEMM_EINVAL, "plan or out is NULL");
+    if (num_workgroups <= 0) return fail(TSGEMM_EINVAL, "num_workgroups must be > 0");
+    tsg::TileScheduler s;
+    s.setup((uint32_t)num_workgroups, (uint32_t)p->m_blocks, (uint32_t)p->n_blocks, (uint32_t)p->group);
+    int64_t row = 0;
+    for (uint32_t wid = 0; wid < (uint32_t)num_workgroups; ++wid)
+        for (s.init(wid); s.valid(); s.next_tile(), ++row) {
+            out[4 * row + 0] = (int32_t)wid;
+            out[4 * row + 1] = (int32_t)s.iter;
+            out[4 * row + 2] = (int32_t)s.m_idx;
+            out[4 * row + 3] = (int32_t)s.n_idx;
+        }
+    if (row != p->tiles) return fail(TSGEMM_EINVAL, "schedule covered %lld of %lld tiles", (long long)row, (long long)p->tiles);
+    return TSGEMM_OK;
+}
+
+int tsgemm_dump_schedule(const tsgemm_plan* p, int32_t* out) {
+    g_err[0] = '\0';
+    if (!p || !out) return fail(TSGEMM_EINVAL, "plan or out is NULL");
+    if (p->tiles == 0) return TSGEMM_OK;
+    Grid g;
+    int rc = resolve_grid(p, &g);
+    if (rc != TSGEMM_OK) return rc;
+    const size_t n = (size_t)g.P * g.max_iters * 4;
+    int32_t* d = nullptr;
+    hipError_t e = hipMalloc(&d, n * sizeof(int32_t));
+    if (e != hipSuccess) return fail(TSGEMM_ENOMEM, "hipMalloc: %s", hipGetErrorString(e));
+    std::vector<int32_t> h(n);
+    e = hipMemset(d, 0xFF, n * sizeof(int32_t));
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(tsg::tsgemm_schedule_kernel, dim3(g.P), dim3(64), 0, 0, g.P, (uint32_t)p->m_blocks,
+                           (uint32_t)p->n_blocks, (uint32_t)p->group, g.xcds, g.max_iters, d);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipMemcpy(h.data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost);
+    hipError_t e2 = hipFree(d);
+    if (e != hipSuccess) return fail(TSGEMM_EHIP, "schedule kernel: %s", hipGetErrorString(e));
+    if (e2 != hipSuccess) return fail(TSGEMM_EHIP, "hipFree: %s", hipGetErrorString(e2));
+    // rows are stored at [worker][iter]: reading them in that order sorts them
+    int64_t row = 0;
+    for (size_t i = 0; i < n; i += 4) {
+        if (h[i] < 0) continue;
+        if (row >= p->tiles) return fail(TSGEMM_EINVAL, "device schedule visited more than %lld tiles", (long long)p->tiles);
+        std::memcpy(out + 4 * row, &h[i], 4 * sizeof(int32_t));
+        ++row;
+    }
+    if (row != p->tiles) return fail(TSGEMM_EINVAL, "device schedule visited %lld of %lld tiles", (long long)row, (long long)p->tiles);
+    return TSGEMM_OK;
+}
+
+void tsgemm_destroy(tsgemm_plan* p) { delete p; }
+
+}  // extern "C"

@@ -1,0 +1,443 @@
+// Persistent, tile-scheduled GEMM kernel for gfx950 (CDNA4).
+//
+//   C[M,N] = A[M,K] * B[K,N], fp16/bf16 in and out, fp32 accumulation.
+//
+// Method (page "[Feature] Introduce tile scheduler #2441", diff of
+// examples/gemm_sm100/gemm_tcgen5mma_ws_persistent.py, gemm_persistent):
+//   * a fixed grid of persistent workers; each runs one `while sched.valid()`
+//     loop over its tiles (tile_scheduler.h);
+//   * the K loop streams A and B slabs through a ring of shared-memory stages:
+//     slab counter phase = w * k_blocks + k runs across tiles, stage
+//     phase % stages (the review on the page's conversation tab settles the
+//     slot index as phase % num_stages);
+//   * the MMA accumulates the tile in fp32, clearing the accumulator on k == 0;
+//   * the epilogue casts the fp32 tile to the output type and stores it.
+// The page's SM100 design (TMA, tcgen05 into TMEM, mbarriers, one warp per
+// role) is replaced by what gfx950 offers:
+//   * loads: buffer_load ... lds (16 bytes per lane straight into LDS) with a
+//     per-slab buffer descriptor whose range check returns zero past the matrix
+//     edge (the analogue of TMA's out-of-bounds fill);
+//   * the loader runs `stages - 1` slabs ahead of the math with its own
+//     scheduler copy, so the next tile's first slabs are in flight while the
+//     current tile's epilogue stores drain;
+//   * math: v_mfma_f32_16x16x32_{f16,bf16}; A fragments come from
+//     K-contiguous LDS rows (ds_read_b128), B fragments from N-contiguous LDS
+//     rows through the LDS transpose read ds_read_b64_tr_b16;
+//   * LDS rows are XOR-swizzled in 16-byte chunks so fragment reads spread over
+//     the banks; the swizzle is applied on the global side of the DMA (each
+//     lane fetches the chunk that belongs at its fixed LDS position);
+//   * 256 threads = 4 wavefronts in a 2x2 grid, one per SIMD; every wave
+//     computes a (BM/2) x (BN/2) sub-tile with its accumulators in registers;
+//   * the MFMA is issued with B as its first operand, so a lane's results run
+//     along N and the epilogue writes 16 contiguous bytes per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "tile_scheduler.h"
+
+namespace tsg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+enum { DT_FP16 = 1, DT_BF16 = 2 };
+constexpr int kThreads = 256;
+constexpr uint32_t kRawBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+struct GemmArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* C;
+    int32_t* trace;  // optional (worker, iter, m, n) per processed tile
+    int64_t M, N, K;
+    uint32_t m_blocks, n_blocks, k_blocks, group;
+    uint32_t P, max_iters, num_xcd;
+};
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(i16x8 a, i16x8 b, f32x4 c) {
+    if constexpr (DT == DT_FP16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> one dword of two 16-bit values (low half = a), round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    uint32_t r;
+    if constexpr (DT == DT_FP16)
+        asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    else
+        asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kRawBufferFlags);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// All LDS reads of this wave done, then workgroup barrier.  The asm is a
+// compiler memory barrier too, so no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int DT, int BM, int BN, int BK, int L>
+struct GemmTraits {
+    static constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
+    static constexpr int FM = WM / 16, FN = WN / 16;        // 16x16 blocks per wave
+    static constexpr int KS = BK / 32;                      // MFMA k-steps per slab
+    static constexpr int CA = BK / 8;                       // 16-byte chunks per A row
+    static constexpr int CB = BN / 8;                       // 16-byte chunks per B row
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = STAGE * L;
+    static constexpr int NA = A_BYTES / (1024 * 4);         // DMA instructions per wave, A
+    static constexpr int NB = B_BYTES / (1024 * 4);         // DMA instructions per wave, B
+    static constexpr int NL = NA + NB;
+    static_assert(BK == 32 || BK == 64, "block_K");
+    static_assert(FN % 2 == 0 && FM >= 1, "wave tile");
+    static_assert(NA >= 1 && NB >= 1, "slab too small for 4 waves");
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(CB >= 16, "B swizzle needs 16 chunks per row");
+};
+
+// Swizzled 16-byte chunk slot of logical chunk c in LDS row r.
+template <int CA>
+__device__ __forceinline__ uint32_t swz_a(uint32_t r) {
+    // 8 consecutive rows at one logical chunk land on 8 distinct bank groups
+    return CA == 8 ? (r & 7u) : ((r >> 1) & 3u);
+}
+__device__ __forceinline__ uint32_t swz_b(uint32_t kr) {
+    // the 4 rows of one transpose read, and the two row octets a wave reads
+    // together, land on distinct bank groups
+    const uint32_t s = (kr & 1u) | ((kr & 2u) << 1);  // 0,1,4,5 for kr%4 = 0..3
+    return s | (((kr >> 3) & 1u) << 3);
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// One 16-byte-per-lane DMA from a buffer into LDS.  Issued as inline asm so the
+// compiler does not treat every later LDS read as dependent on it (it cannot
+// tell the stage being filled from the stage being read); the kernel waits on
+// vmcnt itself before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+    asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    // all four words are wave-uniform; readfirstlane keeps them in SGPRs
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));  // stride 0
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = (int)kRawBufferFlags;
+    return r;
+}
+
+template <int DT, int BM, int BN, int BK, int L>
+__global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
+    using T = GemmTraits<DT, BM, BN, BK, L>;
+    constexpr int FM = T::FM, FN = T::FN, KS = T::KS, NA = T::NA, NB = T::NB, NL = T::NL;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem);
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wr = wave >> 1, wc = wave & 1u;  // wave row / column in the 2x2 grid
+    const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K;
+    const uint32_t k_blocks = args.k_blocks;
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
+
+    // ---- per-lane DMA source offsets (bytes from the slab origin) ----
+    uint32_t voff[NL];
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+        const uint32_t p = (wave * NA + q) * 64u + lane;  // 16-byte position in the A stage
+        const uint32_t r = p / T::CA, s = p % T::CA;
+        voff[q] = (r * K + (s ^ swz_a<T::CA>(r)) * 8u) * 2u;
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        const uint32_t p = (wave * NB + q) * 64u + lane;  // 16-byte position in the B stage
+        const uint32_t kr = p / T::CB, s = p % T::CB;
+        voff[NA + q] = (kr * N + (s ^ swz_b(kr)) * 8u) * 2u;
+    }
+
+    // ---- per-lane LDS read offsets (bytes from the stage origin) ----
+    const uint32_t l16 = lane & 15u, lg = lane >> 4;
+    uint32_t a_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        a_off[ks] = (wr * T::WM + l16) * (BK * 2) + (((uint32_t)ks * 4u + lg) ^ swz_a<T::CA>(l16)) * 16u;
+    // B fragments: the n columns of a pair of 16x16 blocks (2t, 2t+1) are
+    // interleaved so that a lane ends up holding 8 consecutive n of one row:
+    // block b, lane group g holds n = 32t + 8g + 4*(b ^ (g & 1)) + 0..3.  A
+    // transpose-read lane with chunk offset q = l16 & 3 therefore reads the
+    // half (b ^ (q & 1)) of its chunk, which also spreads one read's 16 lanes
+    // over 16 distinct bank pairs.
+    uint32_t b_off[FN];
+    {
+        const uint32_t kr0 = 8u * lg + (l16 >> 2);  // k row of the transpose read (ks=0, h=0)
+        const uint32_t sw = swz_b(kr0);
+#pragma unroll
+        for (int t = 0; t < FN / 2; ++t) {
+            const uint32_t chunk = (wc * T::WN + 32u * t) / 8u + (l16 & 3u);
+            const uint32_t base = T::A_BYTES + kr0 * (BN * 2) + (chunk ^ sw) * 16u;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) b_off[2 * t + b] = base + 8u * ((uint32_t)b ^ (l16 & 1u));
+        }
+    }
+
+    // ---- loader: its own scheduler copy, L slabs ahead of the MMA ----
+    TileScheduler ld;
+    ld.setup(args.P, args.m_blocks, args.n_blocks, args.group);
+    ld.init(wid);
+    uint32_t ld_k = 0, ld_phase = 0;
+    i32x4 rs_a, rs_b;
+    uint32_t dma_lds = 0;
+
+    // descriptors and LDS target for the loader's next slab, then advance it;
+    // past the end the descriptors have zero range (the DMA writes zeros
+    // into a stage nobody reads) so every slab issues the same instructions
+    auto next_slab = [&]() __attribute__((always_inline)) {
+        dma_lds = lds_base + (ld_phase % L) * T::STAGE + wave * NA * 1024u;
+        const bool live = k_blocks != 0 && ld.valid();
+        const int64_t m0 = live ? (int64_t)ld.m_idx * BM : 0, n0 = live ? (int64_t)ld.n_idx * BN : 0;
+        const int64_t k0 = (int64_t)ld_k * BK;
+        const int64_t a_left = ((args.M - m0) * args.K - k0) * 2, a_cap = (int64_t)BM * args.K * 2;
+        const int64_t b_left = ((args.K - k0) * args.N - n0) * 2, b_cap = (int64_t)BK * args.N * 2;
+        const uint32_t a_bytes = live ? (uint32_t)(a_left < a_cap ? a_left : a_cap) : 0u;
+        const uint32_t b_bytes = live ? (uint32_t)(b_left < b_cap ? b_left : b_cap) : 0u;
+        rs_a = rsrc_words(args.A + (m0 * args.K + k0) * live, a_bytes);
+        rs_b = rsrc_words(args.B + (k0 * args.N + n0) * live, b_bytes);
+        if (live && ++ld_k == k_blocks) {
+            ld_k = 0;
+            ld.next_tile();
+        }
+        ++ld_phase;
+    };
+    auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        if constexpr (q < NA)
+            dma16(dma_lds + q * 1024u, voff[q], rs_a);
+        else
+            dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u, voff[q], rs_b);
+    };
+
+    // ---- fragments: two register sets, the one in use and the one being filled ----
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i16x8 fa[2][FM];
+    i16x4 fb[2][FN][2];
+
+    // read op r of a k-step into set SET: A block 0, then all B halves, then A blocks 1..
+    auto read_op = [&](auto set_c, auto ks_c, auto r_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_c)::value, KSN = decltype(ks_c)::value, r = decltype(r_c)::value;
+        const uint8_t* base = smem + st;
+        if constexpr (r == 0 || r > 2 * FN) {
+            constexpr int fm = r == 0 ? 0 : r - 2 * FN;
+            fa[SET][fm] = __builtin_bit_cast(i16x8, *(const u32x4*)(base + a_off[KSN] + fm * 16 * (BK * 2)));
+        } else {
+            constexpr int fn = (r - 1) / 2, h = (r - 1) % 2;
+            fb[SET][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(base + b_off[fn] + KSN * 32 * (BN * 2) + h * 4 * (BN * 2)));
+        }
+    };
+    constexpr int R = FM + 2 * FN;
+    auto read_all = [&](auto set_c, auto ks_c, uint32_t st) __attribute__((always_inline)) {
+        static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, ks_c, r_c, st); });
+    };
+
+    // One 32-deep k-step: FM*FN MFMAs from register set CUR (accumulating into
+    // tiles that the epilogue left at zero: the k == 0 clear), with the memory
+    // operations for what follows spread between them.  LAST (the slab's last
+    // k-step) first waits for the next slab and passes the workgroup barrier,
+    // then issues the DMA of slab phase+L into the stage just consumed and
+    // reads the next slab's first k-step; otherwise it reads k-step KSN of the
+    // current stage.
+    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c) __attribute__((always_inline)) {
+        constexpr int CUR = decltype(cur_c)::value;
+        constexpr bool SAME = decltype(same_c)::value;  // refill CUR after its MFMAs (odd tail slab)
+        constexpr int NXT = SAME ? CUR : 1 - CUR;
+        constexpr bool LAST = decltype(last_c)::value;
+        if constexpr (LAST) next_slab();  // scalar only; the DMA itself waits for the barrier
+        constexpr int NSTEP = FM * FN;
+        constexpr int S0 = LAST ? 2 : 0;                  // MFMAs issued before the barrier
+        constexpr int D = LAST ? NL : 0;
+        constexpr int Q = D + (SAME ? 0 : R);
+        constexpr int AVAIL = NSTEP - S0 > 4 ? NSTEP - S0 - 2 : NSTEP - S0;
+        constexpr int PER = (Q + AVAIL - 1) / AVAIL;
+        static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            constexpr int fm = s / FN, fn = s % FN;
+            const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[fm][fn] = mfma16x16x32<DT>(bv, fa[CUR][fm], acc[fm][fn]);
+            if constexpr (LAST && s == S0 - 1) {
+                wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
+                lds_barrier();                                       // ... for every wave; stage phase free
+            }
+            if constexpr (s >= S0) {
+                constexpr int q0 = (s - S0) * PER;
+                constexpr int q1 = q0 + PER < Q ? q0 + PER : Q;
+                static_for<q0, q1>([&](auto q_c) __attribute__((always_inline)) {
+                    constexpr int q = decltype(q_c)::value;
+                    if constexpr (q < D)
+                        dma_op(std::integral_constant<int, q>{});
+                    else
+                        read_op(std::integral_constant<int, NXT>{}, ksn_c, std::integral_constant<int, q - D>{}, read_st);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (SAME) read_all(cur_c, ksn_c, read_st);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using TRUE_ = std::integral_constant<bool, true>;
+    using FALSE_ = std::integral_constant<bool, false>;
+
+    // ---- epilogue: cast and store one finished tile, then clear its
+    // accumulators for the next (the k == 0 clear).  Conversions are volatile
+    // asm so each stays next to its store instead of all being hoisted.  Lanes
+    // outside C get a vector offset past the descriptor's range and are
+    // dropped; the row block goes into the scalar offset.
+    TileScheduler sched;
+    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group);
+    const bool swap = (lg & 1u) != 0;  // odd lane groups hold the upper four columns of block 2t
+    const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
+    const uint32_t lane_off = (row0 * N + col0) * 2u;
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
+        if (args.trace != nullptr && threadIdx.x == 0) {
+            int32_t* row = args.trace + 4 * ((size_t)wid * args.max_iters + sched.iter);
+            *(int4*)row = make_int4((int)wid, (int)sched.iter, (int)m_idx, (int)n_idx);
+        }
+        const int64_t m0 = (int64_t)m_idx * BM, n0 = (int64_t)n_idx * BN;
+        const uint32_t rows_left = (uint32_t)((args.M - m0) < BM ? (args.M - m0) : BM);
+        const uint32_t cols_left = (uint32_t)((args.N - n0) < BN ? (args.N - n0) : BN);
+        const uint32_t c_bytes = ((rows_left - 1u) * N + cols_left) * 2u;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(args.C + (m0 * args.N + n0), c_bytes);
+        static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) {
+            constexpr int fm = decltype(fm_c)::value;
+            const bool row_ok = row0 + fm * 16 < rows_left;
+            static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
+                constexpr int t = decltype(t_c)::value;
+                const f32x4 x = acc[fm][2 * t], y = acc[fm][2 * t + 1];
+                const uint32_t x0 = cvt_pk<DT>(x[0], x[1]), x1 = cvt_pk<DT>(x[2], x[3]);
+                const uint32_t y0 = cvt_pk<DT>(y[0], y[1]), y1 = cvt_pk<DT>(y[2], y[3]);
+                const u32x4 v = swap ? u32x4{y0, y1, x0, x1} : u32x4{x0, x1, y0, y1};
+                const bool ok = row_ok && col0 + 32u * t < cols_left;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (ok ? lane_off : 0x80000000u) + t * 64,
+                                                       fm * 16 * N * 2, 0);
+                acc[fm][2 * t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc[fm][2 * t + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    };
+
+    // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
+    for (int s = 0; s < L; ++s) {
+        next_slab();
+        static_for<0, NL>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+    }
+    wait_vm<(L - 1) * NL < 63 ? (L - 1) * NL : 63>();
+    lds_barrier();
+    read_all(I0{}, I0{}, 0u);
+
+    // Each slab's last k-step publishes the next slab and reads its first
+    // fragments into the other register set.  Two k-steps per slab: sets 0/1
+    // alternate inside the slab.  One k-step per slab: slabs go in pairs; an
+    // odd last slab refills set 0 after its MFMAs so every tile starts on set 0.
+    uint32_t phase = 0;
+    for (sched.init(wid); sched.valid(); sched.next_tile()) {
+        if constexpr (KS == 2) {
+            for (uint32_t k = 0; k < k_blocks; ++k, ++phase) {
+                const uint32_t st_cur = (phase % L) * T::STAGE;
+                const uint32_t st_next = ((phase + 1u) % L) * T::STAGE;
+                kstep(I0{}, FALSE_{}, I1{}, st_cur, FALSE_{});
+                kstep(I1{}, TRUE_{}, I0{}, st_next, FALSE_{});
+            }
+        } else {
+            uint32_t k = 0;
+            for (; k + 1u < k_blocks; k += 2u, phase += 2u) {
+                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{});
+                kstep(I1{}, TRUE_{}, I0{}, ((phase + 2u) % L) * T::STAGE, FALSE_{});
+            }
+            if (k < k_blocks) {
+                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, TRUE_{});
+                ++phase;
+            }
+        }
+        epilogue();
+    }
+    wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
+}
+
+// C = 0 when K == 0 (an empty sum): plain 16-byte stores, N % 8 == 0.
+__global__ void tsgemm_zero_kernel(uint16_t* C, int64_t count8) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count8) *(u32x4*)(C + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Schedule dump: the same scheduler and worker numbering as the GEMM kernel.
+__global__ void tsgemm_schedule_kernel(uint32_t P, uint32_t m_blocks, uint32_t n_blocks,
+                                       uint32_t group, uint32_t num_xcd, uint32_t max_iters,
+                                       int32_t* out) {
+    if (threadIdx.x != 0) return;
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, P, num_xcd);
+    TileScheduler s;
+    s.setup(P, m_blocks, n_blocks, group);
+    for (s.init(wid); s.valid(); s.next_tile()) {
+        int32_t* row = out + 4 * ((size_t)wid * max_iters + s.iter);
+        *(int4*)row = make_int4((int)wid, (int)s.iter, (int)s.m_idx, (int)s.n_idx);
+    }
+}
+
+}  // namespace tsg

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+function include/tsgemm.h declares; create() validates its arguments; plan
+arithmetic; and the scheduler code compiled for the host reproduces the
+oracle schedule bit for bit."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import persistent_tile_scheduled_amd as tsg
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "tsgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsgemm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tsg.load()
+    declared = _header_functions()
+    assert set(declared) == set(tsg.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("args,code,needle", [
+    ((512, 512, 512, 3, 128, 128, 64, 2, 2), tsg.EINVAL, "dtype"),
+    ((-1, 512, 512, 1, 128, 128, 64, 2, 2), tsg.EINVAL, ">= 0"),
+    ((512, 512, 500, 1, 128, 128, 64, 2, 2), tsg.EINVAL, "multiple of block_K"),
+    ((512, 500, 512, 1, 128, 128, 64, 2, 2), tsg.EINVAL, "divisible by 8"),
+    ((512, 512, 512, 1, 128, 128, 64, 0, 2), tsg.EINVAL, "group_size"),
+    ((512, 512, 512, 1, 128, 128, 64, 2, 1), tsg.EINVAL, "num_stages"),
+    ((512, 512, 512, 1, 64, 64, 64, 2, 2), tsg.EUNSUPPORTED, "not compiled"),
+    ((512, 512, 512, 1, 128, 256, 64, 2, 2), tsg.EUNSUPPORTED, "not compiled"),
+    ((1 << 31, 512, 512, 1, 128, 128, 64, 2, 2), tsg.EINVAL, "2^31"),
+    ((512, 512, 1 << 23, 1, 256, 256, 64, 2, 2), tsg.EUNSUPPORTED, "exceeds 2^31"),
+])
+def test_create_rejects(args, code, needle):
+    lib = tsg.load()
+    h = lib.tsgemm_create(*args)
+    assert not h
+    assert needle in tsg.last_error()
+
+
+def test_null_plan_calls_fail_cleanly():
+    lib = tsg.load()
+    assert lib.tsgemm_num_tiles(None) == tsg.EINVAL
+    assert lib.tsgemm_set_num_workgroups(None, 4) == tsg.EINVAL
+    assert lib.tsgemm_run(None, None, None, None, None) == tsg.EINVAL
+    assert "NULL" in tsg.last_error()
+    lib.tsgemm_destroy(None)
+
+
+def test_run_rejects_bad_pointers_before_any_launch():
+    plan = tsg.Plan(256, 256, 256, "fp16", 128, 128, 64, 2, 2, num_workgroups=4)
+    lib = tsg.load()
+    assert lib.tsgemm_run(plan._h, 16, 32, None, None) == tsg.EINVAL       # C NULL
+    assert lib.tsgemm_run(plan._h, 16, 0, 48, None) == tsg.EINVAL          # B NULL
+    assert lib.tsgemm_run(plan._h, 16, 32, 50, None) == tsg.EINVAL         # misaligned
+    assert "aligned" in tsg.last_error()
+    # M*N == 0: nothing to do, succeeds without touching pointers
+    empty = tsg.Plan(0, 256, 256, "fp16", 128, 128, 64, 2, 2, num_workgroups=4)
+    assert lib.tsgemm_run(empty._h, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_plan_info_matches_workload(name):
+    w = WORKLOADS[name]
+    plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
+                    w.num_stages, num_workgroups=w.num_workgroups or 256)
+    inf = plan.info()
+    mb, nb = -(-w.M // w.block_M), -(-w.N // w.block_N)
+    assert (inf["m_blocks"], inf["n_blocks"], inf["k_blocks"]) == (mb, nb, w.K // w.block_K)
+    assert inf["num_tiles"] == mb * nb == plan.num_tiles
+    P = w.num_workgroups or 256
+    assert inf["num_workgroups"] == P and inf["waves"] == -(-mb * nb // P)
+    stage = (w.block_M * w.block_K + w.block_K * w.block_N) * 2
+    assert inf["stage_bytes"] == stage
+    assert inf["lds_slots"] == min(w.num_stages, 160 * 1024 // stage, 4)
+    assert inf["lds_bytes"] <= 160 * 1024 and inf["lds_slots"] >= 2
+
+
+def test_sm90_stage_arithmetic():
+    """The page's lowered sm_90 GEMM (128x128x32 fp16, 3 stages) reserves 49152 bytes
+    of dynamic shared memory: 3 * (128*32 + 32*128) * 2.  Same shape here."""
+    plan = tsg.Plan(1024, 1024, 1024, "fp16", 128, 128, 32, 4, 3, num_workgroups=256)
+    inf = plan.info()
+    assert inf["stage_bytes"] * 3 == 49152 and inf["lds_bytes"] == 49152
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_host_schedule_matches_oracle(name):
+    w = WORKLOADS[name]
+    P = w.num_workgroups or 256
+    plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size, w.num_stages)
+    got = plan.schedule_host(P)
+    mb, nb = -(-w.M // w.block_M), -(-w.N // w.block_N)
+    want = np.array(oracle.schedule.schedule(P, mb, nb, w.group_size), dtype=np.int32)
+    assert np.array_equal(got, want)
+
+
+def test_host_schedule_sweep_partial_groups():
+    rng = np.random.default_rng(5)
+    for _ in range(60):
+        mb, nb = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        gs, P = int(rng.integers(1, 14)), int(rng.integers(1, 40))
+        plan = tsg.Plan(mb * 128, nb * 128, 64, "bf16", 128, 128, 64, gs, 2)
+        want = np.array(oracle.schedule.schedule(P, mb, nb, gs), dtype=np.int32)
+        assert np.array_equal(plan.schedule_host(P), want), (mb, nb, gs, P)

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerance (from the problem statement of the persistent tile-scheduled GEMM):
+elementwise |C - Cref| <= 2e-3 * (|Cref| + 1) and relative Frobenius error
+<= 1e-3, with Cref the oracle's fp64 sum rounded once to the output dtype.
+Schedules (device dump and the GEMM kernel's own trace) must match the oracle
+bit for bit.  Sizes the oracle finishes in seconds are compared element by
+element; the full-size shapes are compared on sampled outputs computed one by
+one, plus whole-matrix properties (every element written, guard bands intact).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import persistent_tile_scheduled_amd as tsg
+from workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+FMT = {"fp16": oracle.FP16, "bf16": oracle.BF16}
+TDT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    return torch.from_numpy(bits.view(np.int16)).view(TDT[dtype]).double().numpy()
+
+
+def _check_close(got: np.ndarray, ref: np.ndarray, what: str):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output (unwritten tile?)"
+    err = np.abs(got - ref)
+    bound = 2e-3 * (np.abs(ref) + 1.0)
+    bad = np.argwhere(err > bound)
+    assert len(bad) == 0, f"{what}: {len(bad)} elements out of tolerance, first {bad[:5].tolist()}, max err {err.max()}"
+    fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert fro <= 1e-3, f"{what}: relative Frobenius error {fro}"
+    return err.max(), fro
+
+
+def _run(plan, A, B, dtype, guard=0, fill=float("nan")):
+    """Run on the GPU; C sits inside a larger buffer with `guard` sentinel
+    elements after it, returned for checking."""
+    M, N = plan.M, plan.N
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    buf = torch.full((M * N + guard,), fill, dtype=TDT[dtype], device=DEV)
+    C = buf[: M * N].view(M, N)
+    plan.run(Ad, Bd, C)
+    torch.cuda.synchronize()
+    return C.cpu(), buf[M * N:].cpu()
+
+
+def _full_check(M, N, K, dtype, dist, seed, bm, bn, bk, gs, S, P=0, xcd=True):
+    A, B = make_inputs(M, N, K, dtype, dist, seed)
+    plan = tsg.Plan(M, N, K, dtype, bm, bn, bk, gs, S, num_workgroups=P, xcd_remap=xcd)
+    C, guard = _run(plan, A, B, dtype, guard=64)
+    assert torch.isnan(guard.float()).all(), "write past the end of C"
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[dtype])
+    return _check_close(C.double().numpy(), _bits_to_f64(ref_bits, dtype), f"{M}x{N}x{K} {dtype}")
+
+
+# ---------------------------------------------------------------- small / ragged
+@pytest.mark.parametrize("cfg", ["cfg1_512_fp16", "cfg2_1024_fp16"])
+def test_small_workloads_full_compare(cfg):
+    w = WORKLOADS[cfg]
+    print(f"[case] {cfg}", flush=True)
+    _full_check(w.M, w.N, w.K, w.dtype, w.dist, w.seed, w.block_M, w.block_N, w.block_K,
+                w.group_size, w.num_stages, P=w.num_workgroups)
+
+
+TILES = [(128, 128, 32), (128, 128, 64), (256, 256, 32), (256, 256, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("S", [2, 3, 4])
+def test_ragged_shapes_every_kernel(dtype, tile, S):
+    bm, bn, bk = tile
+    # several tiles with ragged row and column tails; K gives an odd slab count
+    M, N, K = 2 * bm + bm // 2 + 8, 2 * bn + 24, 7 * bk
+    print(f"[case] ragged {dtype} {tile} S={S} {M}x{N}x{K}", flush=True)
+    dist = "uniform" if dtype == "fp16" else "normal_sqrtk"
+    _full_check(M, N, K, dtype, dist, 100 + S, bm, bn, bk, 2, S, P=3)
+
+
+@pytest.mark.parametrize("P", [1, 2, 5, 8, 64, 300])
+def test_worker_counts(P):
+    print(f"[case] P={P}", flush=True)
+    _full_check(640, 768, 384, "bf16", "normal_sqrtk", 200 + P, 128, 128, 64, 3, 2, P=P)
+
+
+def test_xcd_remap_off_matches():
+    print("[case] xcd off", flush=True)
+    _full_check(1024, 1024, 256, "fp16", "uniform", 300, 128, 128, 32, 4, 3, P=0, xcd=False)
+
+
+def test_tiny_and_single_tile():
+    print("[case] tiny", flush=True)
+    _full_check(8, 8, 64, "fp16", "uniform", 301, 128, 128, 64, 1, 2, P=1)
+    _full_check(1, 16, 32, "bf16", "uniform", 302, 256, 256, 32, 1, 4)
+    _full_check(256, 256, 64, "bf16", "uniform", 303, 256, 256, 64, 8, 2)
+
+
+def test_k_zero_and_empty():
+    print("[case] K=0", flush=True)
+    plan = tsg.Plan(300, 264, 0, "fp16", 128, 128, 32, 2, 2)
+    A = torch.empty((300, 0), dtype=torch.float16, device=DEV)
+    B = torch.empty((0, 264), dtype=torch.float16, device=DEV)
+    C = torch.full((300, 264), float("nan"), dtype=torch.float16, device=DEV)
+    plan.run(A, B, C)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(C.float()).item() == 0
+    plan0 = tsg.Plan(0, 264, 64, "fp16", 128, 128, 32, 2, 2)
+    plan0.run(torch.empty((0, 64), dtype=torch.float16, device=DEV),
+              torch.zeros((64, 264), dtype=torch.float16, device=DEV),
+              torch.empty((0, 264), dtype=torch.float16, device=DEV))
+
+
+# ---------------------------------------------------------------- exact cases
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_identity_and_permutation_exact(dtype):
+    print(f"[case] exact {dtype}", flush=True)
+    K, N = 512, 384
+    _, B = make_inputs(K, N, K, dtype, "uniform", 400)
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(4))
+    P = torch.zeros((K, K), dtype=TDT[dtype])
+    P[torch.arange(K), perm] = 1
+    plan = tsg.Plan(K, N, K, dtype, 128, 128, 64, 2, 2)
+    C, _ = _run(plan, P, B, dtype)
+    assert torch.equal(C.view(torch.int16), B[perm].view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_output_rounding_is_nearest_even(dtype):
+    """C[i, j] = 1 + (2j+1) * 2^-(p) exactly (p = 11 fp16 / 8 bf16): every value sits
+    half way between two neighbours, so only ties-to-even gives the oracle's bits."""
+    print(f"[case] rounding {dtype}", flush=True)
+    p = 11 if dtype == "fp16" else 8
+    M, N, K = 128, 128, 64
+    A = torch.zeros((M, K), dtype=torch.float64)
+    B = torch.zeros((K, N), dtype=torch.float64)
+    A[:, 0] = 1.0
+    B[0, :] = 1.0
+    A[:, 1] = 2.0 ** -p
+    B[1, :] = torch.tensor([float((2 * (j % 8) + 1)) for j in range(N)])
+    A, B = A.to(TDT[dtype]), B.to(TDT[dtype])
+    plan = tsg.Plan(M, N, K, dtype, 128, 128, 64, 1, 2)
+    C, _ = _run(plan, A, B, dtype)
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[dtype])
+    assert np.array_equal(C.view(torch.int16).numpy().view(np.uint16), ref_bits)
+
+
+# ---------------------------------------------------------------- schedule
+def _plan_for(w, P=None):
+    return tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
+                    w.num_stages, num_workgroups=w.num_workgroups if P is None else P)
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_schedule_dump_bit_exact(cfg):
+    w = WORKLOADS[cfg]
+    plan = _plan_for(w)
+    P = plan.num_workgroups
+    got = plan.dump_schedule()
+    mb, nb = -(-w.M // w.block_M), -(-w.N // w.block_N)
+    want = np.array(oracle.schedule.schedule(P, mb, nb, w.group_size), dtype=np.int32)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("cfg", ["cfg1_512_fp16", "cfg2_1024_fp16", "cfg4p_16000x4000x4096_fp16"])
+def test_gemm_kernel_trace_matches_oracle(cfg):
+    """The GEMM kernel's own record of the tiles it processed."""
+    w = WORKLOADS[cfg]
+    print(f"[case] trace {cfg}", flush=True)
+    plan = _plan_for(w)
+    P = plan.num_workgroups
+    T = plan.num_tiles
+    iters = -(-T // P)
+    A, B = workload_inputs(w)
+    trace = torch.full((P * iters * 4,), -1, dtype=torch.int32, device=DEV)
+    C = torch.empty((w.M, w.N), dtype=TDT[w.dtype], device=DEV)
+    plan.run_traced(A.to(DEV), B.to(DEV), C, trace)
+    torch.cuda.synchronize()
+    rows = trace.view(-1, 4).cpu().numpy()
+    rows = rows[rows[:, 0] >= 0]
+    mb, nb = -(-w.M // w.block_M), -(-w.N // w.block_N)
+    want = np.array(oracle.schedule.schedule(P, mb, nb, w.group_size), dtype=np.int32)
+    assert np.array_equal(rows, want)
+
+
+# ---------------------------------------------------------------- full size, sampled
+def _sampled_check(w, n_samples=6000, seed=9):
+    A, B = workload_inputs(w)
+    plan = _plan_for(w)
+    guard = 4096
+    C, g = _run(plan, A, B, w.dtype, guard=guard)
+    assert torch.isnan(g.float()).all(), "write past the end of C"
+    Cf = C.float()
+    assert torch.isfinite(Cf).all(), "unwritten or non-finite outputs"
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, w.M, n_samples)
+    cols = rng.integers(0, w.N, n_samples)
+    # plus the last row and column (ragged tails) and tile corners
+    edge_r = np.concatenate([np.full(256, w.M - 1), rng.integers(0, w.M, 256)])
+    edge_c = np.concatenate([rng.integers(0, w.N, 256), np.full(256, w.N - 1)])
+    rows = np.concatenate([rows, edge_r, [0, w.M - 1, 0, w.M - 1]])
+    cols = np.concatenate([cols, edge_c, [0, 0, w.N - 1, w.N - 1]])
+    A64, B64 = A.double().numpy(), B.double().numpy()
+    c64 = oracle.gemm_entries_f64(A64, B64, rows, cols)
+    ref = _bits_to_f64(oracle.round_to(c64, FMT[w.dtype]), w.dtype)
+    got = C.double().numpy()[rows, cols]
+    return _check_close(got, ref, w.name)
+
+
+@pytest.mark.parametrize("cfg", ["cfg3_8192_bf16", "cfg4_16384x4096x4096_fp16",
+                                 "cfg4p_16000x4000x4096_fp16", "cfg5_2048x2048x32768_bf16"])
+def test_full_size_sampled(cfg):
+    print(f"[case] full {cfg}", flush=True)
+    _sampled_check(WORKLOADS[cfg])
+
+
+def test_full_tile_of_8192_exact_compare():
+    """One whole 256x256 output tile of the 8192^3 shape, every element."""
+    w = WORKLOADS["cfg3_8192_bf16"]
+    print("[case] cfg3 tile", flush=True)
+    A, B = workload_inputs(w)
+    plan = _plan_for(w)
+    C, _ = _run(plan, A, B, w.dtype)
+    r0, c0 = 256 * 17, 256 * 29
+    ref_bits, _ = oracle.reference_c(A[r0:r0 + 256].double().numpy(), B[:, c0:c0 + 256].double().numpy(),
+                                     FMT[w.dtype])
+    _check_close(C[r0:r0 + 256, c0:c0 + 256].double().numpy(), _bits_to_f64(ref_bits, w.dtype), "cfg3 tile")
+
+
+def test_deterministic_repeat():
+    """Each tile is owned by one workgroup with a fixed order: runs are bit-identical."""
+    w = WORKLOADS["cfg2_1024_fp16"]
+    A, B = workload_inputs(w)
+    plan = _plan_for(w)
+    C1, _ = _run(plan, A, B, w.dtype)
+    C2, _ = _run(plan, A, B, w.dtype)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
