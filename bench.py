@@ -1,0 +1,145 @@
+"""Benchmark of the persistent tile-scheduled GEMM on one MI355X.
+
+One step = one tsgemm_run over the 8192^3 bf16 workload (A, B i.i.d.
+normal(0,1)/sqrt(K), tiles 256x256x64, group_size 8, 3 stages requested, one
+persistent workgroup per CU).  Inputs are resident in HBM before timing starts.
+Prints one JSON line:
+  value      whole-job TFLOP/s = 2*M*N*K*steps / wall time of the timed steps
+  roofline   the GEMM kernel against the dense bf16 MFMA peak: achieved =
+             2*M*N*K per launch / mean launch time from HIP events recorded on
+             the launch stream around every timed launch
+  cpu_baseline  the CPU oracle (fp64 triple loop) timed on this host on a
+             bounded sample of the same product (its first R rows of C)
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense MFMA, published
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "cfg3_8192_bf16"
+
+
+def cpu_baseline(w, A, B, target_s: float = 12.0):
+    """Time the oracle on the first R rows of C, R sized for ~target_s seconds."""
+    import numpy as np
+    import oracle
+    B64 = B.double().numpy()
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm_f64(A[:rows].double().numpy(), B64)
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-3))))
+    A64 = A[:rows].double().numpy()
+    t0 = time.perf_counter()
+    c = oracle.gemm_f64(A64, B64)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(c).all()
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.M} rows of C ({flops / 1e9:.1f} GFLOP, fp64 triple loop, {dt:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import persistent_tile_scheduled_amd as tsg
+    from workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    A, B = workload_inputs(w)
+    Ad, Bd = A.to(dev), B.to(dev)
+    C = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=dev)
+    plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
+                    w.num_stages, num_workgroups=w.num_workgroups)
+    info = plan.info()
+    P = plan.num_workgroups
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        plan.run(Ad, Bd, C, stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        plan.run(Ad, Bd, C, stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_ms = sum(launch_ms) / len(launch_ms)
+
+    flops = float(w.flops)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    out = {
+        "metric": "GEMM TFLOP/s and % of dense fp16/bf16 MFMA peak, 1xMI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {
+            "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+            "tile": [w.block_M, w.block_N, w.block_K], "group_size": w.group_size,
+            "num_stages": w.num_stages, "lds_slots": info["lds_slots"], "num_workgroups": P,
+            "inputs": f"{w.dist}, seed {w.seed}",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "kernel_ms": {"mean": round(mean_ms, 4), "min": round(launch_ms[0], 4),
+                          "median": round(launch_ms[len(launch_ms) // 2], 4)},
+            "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9, 1),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

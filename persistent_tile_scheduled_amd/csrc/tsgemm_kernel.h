@@ -71,24 +71,29 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------
+// acc += a * b on the 16x16x32 matrix core.  Written as asm with the
+// accumulator constrained to AGPRs: each 16x16 fp32 tile stays in one fixed
+// AGPR quad for the whole kernel and the VGPRs are left to the fragments.
 template <int DT>
-__device__ __forceinline__ f32x4 mfma16x16x32(i16x8 a, i16x8 b, f32x4 c) {
+__device__ __forceinline__ void mfma16x16x32(f32x4& acc, i16x8 a, i16x8 b) {
     if constexpr (DT == DT_FP16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
     else
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// Two fp32 -> one dword of two 16-bit values (low half = a), round to nearest even.
+// Two fp32 accumulators (held in AGPRs) -> one dword of two 16-bit values
+// (low half = a), round to nearest even.  The AGPR reads sit inside the asm so
+// they happen at the store that needs them rather than all up front.
 template <int DT>
 __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
-    uint32_t r;
+    uint32_t r, t;
     if constexpr (DT == DT_FP16)
-        asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+        asm volatile("v_accvgpr_read_b32 %0, %2\n\tv_accvgpr_read_b32 %1, %3\n\tv_cvt_pk_f16_f32 %0, %0, %1"
+                     : "=&v"(r), "=&v"(t) : "a"(a), "a"(b));
     else
-        asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+        asm volatile("v_accvgpr_read_b32 %0, %2\n\tv_accvgpr_read_b32 %1, %3\n\tv_cvt_pk_bf16_f32 %0, %0, %1"
+                     : "=&v"(r), "=&v"(t) : "a"(a), "a"(b));
     return r;
 }
 
@@ -156,12 +161,18 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// One 16-byte-per-lane DMA from a buffer into LDS.  Issued as inline asm so the
-// compiler does not treat every later LDS read as dependent on it (it cannot
-// tell the stage being filled from the stage being read); the kernel waits on
-// vmcnt itself before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-    asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds_addr), "v"(voff), "s"(rsrc)
+// One 16-byte-per-lane DMA from a buffer into LDS at byte offset
+// vlane + uoff (a per-lane part and a wave-uniform part added here, so the
+// compiler keeps one lane register per pattern instead of one per
+// instruction).  Issued as inline asm so the compiler does not treat every
+// later LDS read as dependent on it (it cannot tell the stage being filled
+// from the stage being read); the kernel waits on vmcnt itself before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t vlane, uint32_t uoff, i32x4 rsrc) {
+    uint32_t tmp;
+    asm volatile("v_add_u32 %0, %1, %2\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
+                 : "=&v"(tmp)
+                 : "s"(uoff), "v"(vlane), "s"(rsrc), "{m0}"(lds_addr)
                  : "memory");
 }
 
@@ -190,20 +201,27 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
     const uint32_t k_blocks = args.k_blocks;
     const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
 
-    // ---- per-lane DMA source offsets (bytes from the slab origin) ----
-    uint32_t voff[NL];
+    // ---- DMA source offsets (bytes from the slab origin) = lane part + uniform part ----
+    // Instruction q of this wave fills 16-byte LDS positions p = qe*64 + lane,
+    // qe = wave*NA + q (A) or wave*NB + q (B); the lane fetches the logical
+    // chunk that the swizzle puts at p.  A's swizzle depends on the lane only;
+    // B's also on bits 1 and 3 of the stage row, i.e. on vkey = (qe*64/CB) & 0xA.
+    const uint32_t va = ((lane / T::CA) * K + ((lane % T::CA) ^ swz_a<T::CA>(lane / T::CA)) * 8u) * 2u;
+    uint32_t ua[NA], ub[NB];
 #pragma unroll
-    for (int q = 0; q < NA; ++q) {
-        const uint32_t p = (wave * NA + q) * 64u + lane;  // 16-byte position in the A stage
-        const uint32_t r = p / T::CA, s = p % T::CA;
-        voff[q] = (r * K + (s ^ swz_a<T::CA>(r)) * 8u) * 2u;
-    }
+    for (int q = 0; q < NA; ++q) ua[q] = (wave * NA + q) * (64u / T::CA) * K * 2u;
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-        const uint32_t p = (wave * NB + q) * 64u + lane;  // 16-byte position in the B stage
-        const uint32_t kr = p / T::CB, s = p % T::CB;
-        voff[NA + q] = (kr * N + (s ^ swz_b(kr)) * 8u) * 2u;
+    for (int q = 0; q < NB; ++q) ub[q] = (wave * NB + q) * (64u / T::CB) * N * 2u;
+    uint32_t vb[4];  // indexed by vkey bits (1, 3)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const uint32_t kr = lane / T::CB + ((v & 1) << 1) + ((v >> 1) << 3);
+        vb[v] = ((lane / T::CB) * N + ((lane % T::CB) ^ swz_b(kr)) * 8u) * 2u;
     }
+    auto vb_for = [&](uint32_t qe) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t key = (qe * (64u / T::CB)) & 0xAu;
+        return vb[((key >> 1) & 1u) | ((key >> 3) << 1)];
+    };
 
     // ---- per-lane LDS read offsets (bytes from the stage origin) ----
     const uint32_t l16 = lane & 15u, lg = lane >> 4;
@@ -261,62 +279,66 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int q = decltype(q_c)::value;
         if constexpr (q < NA)
-            dma16(dma_lds + q * 1024u, voff[q], rs_a);
+            dma16(dma_lds + q * 1024u, va, ua[q], rs_a);
         else
-            dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u, voff[q], rs_b);
+            dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u,
+                  vb_for(wave * NB + (q - NA)), ub[q - NA], rs_b);
     };
 
-    // ---- fragments: two register sets, the one in use and the one being filled ----
+    // ---- fragments: A single-buffered (block fm is refilled right after its
+    // last MFMA), B in two sets (every B block is used until the k-step ends) ----
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i16x8 fa[2][FM];
+    i16x8 fa[FM];
     i16x4 fb[2][FN][2];
 
-    // read op r of a k-step into set SET: A block 0, then all B halves, then A blocks 1..
-    auto read_op = [&](auto set_c, auto ks_c, auto r_c, uint32_t st) __attribute__((always_inline)) {
-        constexpr int SET = decltype(set_c)::value, KSN = decltype(ks_c)::value, r = decltype(r_c)::value;
-        const uint8_t* base = smem + st;
-        if constexpr (r == 0 || r > 2 * FN) {
-            constexpr int fm = r == 0 ? 0 : r - 2 * FN;
-            fa[SET][fm] = __builtin_bit_cast(i16x8, *(const u32x4*)(base + a_off[KSN] + fm * 16 * (BK * 2)));
-        } else {
-            constexpr int fn = (r - 1) / 2, h = (r - 1) % 2;
-            fb[SET][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(base + b_off[fn] + KSN * 32 * (BN * 2) + h * 4 * (BN * 2)));
-        }
+    // LDS reads of one k-step: A block fm, and B halves (fn, h) into set SET
+    auto read_a = [&](auto ks_c, auto fm_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int KSN = decltype(ks_c)::value, fm = decltype(fm_c)::value;
+        fa[fm] = __builtin_bit_cast(i16x8, *(const u32x4*)(smem + st + a_off[KSN] + fm * 16 * (BK * 2)));
     };
-    constexpr int R = FM + 2 * FN;
+    auto read_b = [&](auto set_c, auto ks_c, auto r_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_c)::value, KSN = decltype(ks_c)::value, r = decltype(r_c)::value;
+        constexpr int fn = r / 2, h = r % 2;
+        fb[SET][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(smem + st + b_off[fn] + KSN * 32 * (BN * 2) + h * 4 * (BN * 2)));
+    };
+    constexpr int RB = 2 * FN;
     auto read_all = [&](auto set_c, auto ks_c, uint32_t st) __attribute__((always_inline)) {
-        static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, ks_c, r_c, st); });
+        static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) { read_a(ks_c, fm_c, st); });
+        static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(set_c, ks_c, r_c, st); });
     };
 
-    // One 32-deep k-step: FM*FN MFMAs from register set CUR (accumulating into
-    // tiles that the epilogue left at zero: the k == 0 clear), with the memory
-    // operations for what follows spread between them.  LAST (the slab's last
+    // One 32-deep k-step: FM*FN MFMAs (fm-major) from A and B set CUR,
+    // accumulating into tiles that the epilogue left at zero (the k == 0
+    // clear), with the memory operations for what follows between them: A
+    // block fm is refilled right after its last use; the DMA and the B reads
+    // into set NXT are spread over the remaining steps.  LAST (the slab's last
     // k-step) first waits for the next slab and passes the workgroup barrier,
-    // then issues the DMA of slab phase+L into the stage just consumed and
-    // reads the next slab's first k-step; otherwise it reads k-step KSN of the
-    // current stage.
+    // then issues the DMA of slab phase+L into the stage just consumed and reads
+    // the next slab's first k-step; otherwise it reads k-step KSN of the
+    // current stage.  SAME (an odd tail slab) refills B set CUR after its MFMAs.
     auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
-        constexpr bool SAME = decltype(same_c)::value;  // refill CUR after its MFMAs (odd tail slab)
+        constexpr bool SAME = decltype(same_c)::value;
         constexpr int NXT = SAME ? CUR : 1 - CUR;
         constexpr bool LAST = decltype(last_c)::value;
         if constexpr (LAST) next_slab();  // scalar only; the DMA itself waits for the barrier
         constexpr int NSTEP = FM * FN;
         constexpr int S0 = LAST ? 2 : 0;                  // MFMAs issued before the barrier
         constexpr int D = LAST ? NL : 0;
-        constexpr int Q = D + (SAME ? 0 : R);
+        constexpr int Q = D + (SAME ? 0 : RB);
         constexpr int AVAIL = NSTEP - S0 > 4 ? NSTEP - S0 - 2 : NSTEP - S0;
         constexpr int PER = (Q + AVAIL - 1) / AVAIL;
+        static_assert(FN - 1 >= S0, "A refills must follow the barrier");
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / FN, fn = s % FN;
             const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[fm][fn] = mfma16x16x32<DT>(bv, fa[CUR][fm], acc[fm][fn]);
+            mfma16x16x32<DT>(acc[fm][fn], bv, fa[fm]);
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
@@ -329,12 +351,14 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
                     if constexpr (q < D)
                         dma_op(std::integral_constant<int, q>{});
                     else
-                        read_op(std::integral_constant<int, NXT>{}, ksn_c, std::integral_constant<int, q - D>{}, read_st);
+                        read_b(std::integral_constant<int, NXT>{}, ksn_c, std::integral_constant<int, q - D>{}, read_st);
                 });
             }
+            if constexpr (fn == FN - 1) read_a(ksn_c, std::integral_constant<int, fm>{}, read_st);
             __builtin_amdgcn_sched_barrier(0);
         });
-        if constexpr (SAME) read_all(cur_c, ksn_c, read_st);
+        if constexpr (SAME)
+            static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(cur_c, ksn_c, r_c, read_st); });
     };
 
     using I0 = std::integral_constant<int, 0>;
