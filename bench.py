@@ -54,6 +54,29 @@ def cpu_baseline(w, A, B, target_s: float = 12.0):
     }
 
 
+def copy_mode(args, torch):
+    """Plain device-to-device copy of a known size: reads and writes
+    copy-mib MiB per launch.  Its FETCH_SIZE / WRITE_SIZE counter readings give
+    the factor that turns those counters into bytes."""
+    dev = torch.device("cuda:0")
+    n = args.copy_mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "ms_per_launch": round(ms, 4), "GB/s (read+write)": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +84,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["gemm", "copy"], default="gemm",
+                    help="copy: time a plain device copy of --copy-mib MiB (calibrates HBM byte counters)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -68,6 +94,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.mode == "copy":
+        copy_mode(args, torch)
+        return
     import persistent_tile_scheduled_amd as tsg
     from workloads import WORKLOADS, workload_inputs
 

@@ -21,7 +21,7 @@
 namespace {
 
 constexpr int kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
-constexpr int kMaxSlots = 4;           // deepest compiled LDS ring
+constexpr int kMaxSlots = 5;           // deepest compiled LDS ring
 
 thread_local char g_err[512] = "";
 
@@ -48,7 +48,8 @@ struct KernelEntry {
 #define TSG_TILE(DT, BM, BN, BK)                                            \
     {DT, BM, BN, BK, 2, launch<DT, BM, BN, BK, 2>},                         \
     {DT, BM, BN, BK, 3, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 3 <= kLdsBytes) ? 3 : 2>}, \
-    {DT, BM, BN, BK, 4, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 4 <= kLdsBytes) ? 4 : 2>}
+    {DT, BM, BN, BK, 4, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 4 <= kLdsBytes) ? 4 : 2>}, \
+    {DT, BM, BN, BK, 5, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 5 <= kLdsBytes) ? 5 : 2>}
 
 const KernelEntry kKernels[] = {
     TSG_TILE(1, 128, 128, 32), TSG_TILE(1, 128, 128, 64), TSG_TILE(1, 256, 256, 32), TSG_TILE(1, 256, 256, 64),

@@ -55,6 +55,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 enum { DT_FP16 = 1, DT_BF16 = 2 };
+#ifndef TSG_DMA_SPACING
+#define TSG_DMA_SPACING 3
+#endif
+constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA issues
 constexpr int kThreads = 256;
 constexpr uint32_t kRawBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
 
@@ -161,19 +165,12 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// One 16-byte-per-lane DMA from a buffer into LDS at byte offset
-// vlane + uoff (a per-lane part and a wave-uniform part added here, so the
-// compiler keeps one lane register per pattern instead of one per
-// instruction).  Issued as inline asm so the compiler does not treat every
-// later LDS read as dependent on it (it cannot tell the stage being filled
-// from the stage being read); the kernel waits on vmcnt itself before the
-// barrier that publishes a stage.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t vlane, uint32_t uoff, i32x4 rsrc) {
-    uint32_t tmp;
-    asm volatile("v_add_u32 %0, %1, %2\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
-                 : "=&v"(tmp)
-                 : "s"(uoff), "v"(vlane), "s"(rsrc), "{m0}"(lds_addr)
-                 : "memory");
+// One 16-byte-per-lane DMA from a buffer into LDS.  Issued as inline asm so
+// the compiler does not treat every later LDS read as dependent on it (it
+// cannot tell the stage being filled from the stage being read); the kernel
+// waits on vmcnt itself before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
@@ -222,6 +219,13 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
         const uint32_t key = (qe * (64u / T::CB)) & 0xAu;
         return vb[((key >> 1) & 1u) | ((key >> 3) << 1)];
     };
+    // full per-instruction offsets, formed once (an add right before each DMA
+    // would stall its issue on the VALU result)
+    uint32_t voff[NL];
+#pragma unroll
+    for (int q = 0; q < NA; ++q) voff[q] = va + ua[q];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) voff[NA + q] = vb_for(wave * NB + q) + ub[q];
 
     // ---- per-lane LDS read offsets (bytes from the stage origin) ----
     const uint32_t l16 = lane & 15u, lg = lane >> 4;
@@ -279,10 +283,9 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int q = decltype(q_c)::value;
         if constexpr (q < NA)
-            dma16(dma_lds + q * 1024u, va, ua[q], rs_a);
+            dma16(dma_lds + q * 1024u, voff[q], rs_a);
         else
-            dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u,
-                  vb_for(wave * NB + (q - NA)), ub[q - NA], rs_b);
+            dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u, voff[q], rs_b);
     };
 
     // ---- fragments: A single-buffered (block fm is refilled right after its
@@ -295,21 +298,32 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
     i16x8 fa[FM];
     i16x4 fb[2][FN][2];
 
-    // LDS reads of one k-step: A block fm, and B halves (fn, h) into set SET
-    auto read_a = [&](auto ks_c, auto fm_c, uint32_t st) __attribute__((always_inline)) {
-        constexpr int KSN = decltype(ks_c)::value, fm = decltype(fm_c)::value;
-        fa[fm] = __builtin_bit_cast(i16x8, *(const u32x4*)(smem + st + a_off[KSN] + fm * 16 * (BK * 2)));
+    // LDS reads of one k-step: A block fm, and B halves (fn, h) into set SET.
+    // The stage base is folded into per-lane address registers once per
+    // k-step (ra, rb); each read is then register + immediate.
+    uint32_t ra, rb[FN];
+    auto set_addr = [&](auto ks_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int KSN = decltype(ks_c)::value;
+        ra = lds_base + st + a_off[KSN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) rb[fn] = lds_base + st + b_off[fn] + KSN * 32 * (BN * 2);
     };
-    auto read_b = [&](auto set_c, auto ks_c, auto r_c, uint32_t st) __attribute__((always_inline)) {
-        constexpr int SET = decltype(set_c)::value, KSN = decltype(ks_c)::value, r = decltype(r_c)::value;
+    auto read_a = [&](auto fm_c) __attribute__((always_inline)) {
+        constexpr int fm = decltype(fm_c)::value;
+        fa[fm] = __builtin_bit_cast(i16x8, *(const __attribute__((address_space(3))) u32x4*)(
+                                               (__attribute__((address_space(3))) uint8_t*)(uintptr_t)ra + fm * 16 * (BK * 2)));
+    };
+    auto read_b = [&](auto set_c, auto r_c) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_c)::value, r = decltype(r_c)::value;
         constexpr int fn = r / 2, h = r % 2;
         fb[SET][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(smem + st + b_off[fn] + KSN * 32 * (BN * 2) + h * 4 * (BN * 2)));
+            (lds_i16x4*)((__attribute__((address_space(3))) uint8_t*)(uintptr_t)rb[fn] + h * 4 * (BN * 2)));
     };
     constexpr int RB = 2 * FN;
     auto read_all = [&](auto set_c, auto ks_c, uint32_t st) __attribute__((always_inline)) {
-        static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) { read_a(ks_c, fm_c, st); });
-        static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(set_c, ks_c, r_c, st); });
+        set_addr(ks_c, st);
+        static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) { read_a(fm_c); });
+        static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(set_c, r_c); });
     };
 
     // One 32-deep k-step: FM*FN MFMAs (fm-major) from A and B set CUR,
@@ -330,10 +344,15 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
         constexpr int NSTEP = FM * FN;
         constexpr int S0 = LAST ? 2 : 0;                  // MFMAs issued before the barrier
         constexpr int D = LAST ? NL : 0;
-        constexpr int Q = D + (SAME ? 0 : RB);
         constexpr int AVAIL = NSTEP - S0 > 4 ? NSTEP - S0 - 2 : NSTEP - S0;
-        constexpr int PER = (Q + AVAIL - 1) / AVAIL;
+        // DMA issues are spaced DS MFMAs apart: a burst of them right after the
+        // barrier (4 waves at once) would overflow the texture unit's queue and
+        // stall instruction issue, MFMAs included
+        constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
+        constexpr int QB = SAME ? 0 : RB;                 // B reads, spread evenly
+        constexpr int PER = QB ? (QB + AVAIL - 1) / AVAIL : 0;
         static_assert(FN - 1 >= S0, "A refills must follow the barrier");
+        if constexpr (!LAST) set_addr(ksn_c, read_st);
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / FN, fn = s % FN;
@@ -342,23 +361,22 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
+                set_addr(ksn_c, read_st);
             }
             if constexpr (s >= S0) {
-                constexpr int q0 = (s - S0) * PER;
-                constexpr int q1 = q0 + PER < Q ? q0 + PER : Q;
+                constexpr int i = s - S0;
+                if constexpr (D && i % DS == 0 && i / DS < D) dma_op(std::integral_constant<int, i / DS>{});
+                constexpr int q0 = i * PER;
+                constexpr int q1 = q0 + PER < QB ? q0 + PER : QB;
                 static_for<q0, q1>([&](auto q_c) __attribute__((always_inline)) {
-                    constexpr int q = decltype(q_c)::value;
-                    if constexpr (q < D)
-                        dma_op(std::integral_constant<int, q>{});
-                    else
-                        read_b(std::integral_constant<int, NXT>{}, ksn_c, std::integral_constant<int, q - D>{}, read_st);
+                    read_b(std::integral_constant<int, NXT>{}, q_c);
                 });
             }
-            if constexpr (fn == FN - 1) read_a(ksn_c, std::integral_constant<int, fm>{}, read_st);
+            if constexpr (fn == FN - 1) read_a(std::integral_constant<int, fm>{});
             __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (SAME)
-            static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(cur_c, ksn_c, r_c, read_st); });
+            static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(cur_c, r_c); });
     };
 
     using I0 = std::integral_constant<int, 0>;

@@ -83,7 +83,7 @@ def test_plan_info_matches_workload(name):
     assert inf["num_workgroups"] == P and inf["waves"] == -(-mb * nb // P)
     stage = (w.block_M * w.block_K + w.block_K * w.block_N) * 2
     assert inf["stage_bytes"] == stage
-    assert inf["lds_slots"] == min(w.num_stages, 160 * 1024 // stage, 4)
+    assert inf["lds_slots"] == min(w.num_stages, 160 * 1024 // stage, 5)
     assert inf["lds_bytes"] <= 160 * 1024 and inf["lds_slots"] >= 2
 
 

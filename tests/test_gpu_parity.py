@@ -73,7 +73,7 @@ TILES = [(128, 128, 32), (128, 128, 64), (256, 256, 32), (256, 256, 64)]
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("tile", TILES)
-@pytest.mark.parametrize("S", [2, 3, 4])
+@pytest.mark.parametrize("S", [2, 3, 4, 5])
 def test_ragged_shapes_every_kernel(dtype, tile, S):
     bm, bn, bk = tile
     # several tiles with ragged row and column tails; K gives an odd slab count
