@@ -27,6 +27,32 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense MFMA, published
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "cfg3_8192_bf16"
+KERNEL_SOURCES = ("persistent_tile_scheduled_amd/csrc/tsgemm_kernel.h",
+                  "persistent_tile_scheduled_amd/csrc/tile_scheduler.h",
+                  "persistent_tile_scheduled_amd/csrc/tsgemm.hip")
+PROFILE_FOR = {"cfg3_8192_bf16": "profiles/gemm_8192_bf16.md"}
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+    calibrated on a plain copy) as recorded in profiles/, or None when there is
+    no record or the kernel sources changed since it was taken."""
+    import hashlib
+    path = PROFILE_FOR.get(workload)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    for line in open(os.path.join(ROOT, path)):
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            k, v = line.strip().split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, A, B, target_s: float = 12.0):
@@ -158,7 +184,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(w.name),
             "kernel_ms": {"mean": round(mean_ms, 4), "min": round(launch_ms[0], 4),
                           "median": round(launch_ms[len(launch_ms) // 2], 4)},
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9, 1),
