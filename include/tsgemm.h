@@ -91,6 +91,11 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype,
 /* Fix the persistent grid size P (>= 1); 0 restores "one per compute unit". */
 int tsgemm_set_num_workgroups(tsgemm_plan* plan, int num_workgroups);
 
+/* Wavefronts per workgroup: 4 (a 2x2 grid, one per SIMD) or 8 (2x4, two per
+ * SIMD, so one wave's issue stalls leave the matrix core to the other); 0
+ * restores the default for the tile shape.  Results are identical. */
+int tsgemm_set_waves(tsgemm_plan* plan, int waves);
+
 /* Enable (1, default) or disable (0) the XCD-aware workgroup -> worker id
  * permutation.  The schedule is defined on worker ids either way. */
 int tsgemm_set_xcd_remap(tsgemm_plan* plan, int enable);

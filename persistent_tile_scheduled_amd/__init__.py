@@ -28,7 +28,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, -1, -2, -3, -4
 
 # every symbol the header declares
 EXPORTS = (
-    "tsgemm_create", "tsgemm_set_num_workgroups", "tsgemm_set_xcd_remap", "tsgemm_run",
+    "tsgemm_create", "tsgemm_set_num_workgroups", "tsgemm_set_waves", "tsgemm_set_xcd_remap", "tsgemm_run",
     "tsgemm_run_traced", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
 )
@@ -76,6 +76,8 @@ def load(path: str | None = None):
     lib.tsgemm_create.restype = vp
     lib.tsgemm_set_num_workgroups.argtypes = [vp, i32]
     lib.tsgemm_set_num_workgroups.restype = i32
+    lib.tsgemm_set_waves.argtypes = [vp, i32]
+    lib.tsgemm_set_waves.restype = i32
     lib.tsgemm_set_xcd_remap.argtypes = [vp, i32]
     lib.tsgemm_set_xcd_remap.restype = i32
     lib.tsgemm_run.argtypes = [vp, vp, vp, vp, vp]
@@ -118,7 +120,8 @@ class Plan:
     """A validated problem (tsgemm_create).  Immutable once configured."""
 
     def __init__(self, M: int, N: int, K: int, dtype, block_M: int, block_N: int, block_K: int,
-                 group_size: int, num_stages: int, num_workgroups: int = 0, xcd_remap: bool = True):
+                 group_size: int, num_stages: int, num_workgroups: int = 0, xcd_remap: bool = True,
+                 waves: int = 0):
         lib = load()
         self._lib = lib
         dt = _DTYPES.get(dtype)
@@ -135,6 +138,8 @@ class Plan:
         if num_workgroups:
             _check(lib.tsgemm_set_num_workgroups(self._h, num_workgroups))
         _check(lib.tsgemm_set_xcd_remap(self._h, 1 if xcd_remap else 0))
+        if waves:
+            _check(lib.tsgemm_set_waves(self._h, waves))
 
     def __del__(self):
         h = getattr(self, "_h", None)

@@ -35,30 +35,37 @@ int fail(int code, const char* fmt, ...) {
 
 typedef void (*launch_fn)(const tsg::GemmArgs&, unsigned grid, hipStream_t);
 
-template <int DT, int BM, int BN, int BK, int L>
+template <int DT, int BM, int BN, int BK, int L, int WGN>
 void launch(const tsg::GemmArgs& a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((tsg::tsgemm_kernel<DT, BM, BN, BK, L>), dim3(grid), dim3(tsg::kThreads), 0, s, a);
+    hipLaunchKernelGGL((tsg::tsgemm_kernel<DT, BM, BN, BK, L, WGN>), dim3(grid), dim3(64 * 2 * WGN), 0, s, a);
 }
 
 struct KernelEntry {
-    int dt, bm, bn, bk, slots;
+    int dt, bm, bn, bk, slots, waves;
     launch_fn fn;
 };
 
-#define TSG_TILE(DT, BM, BN, BK)                                            \
-    {DT, BM, BN, BK, 2, launch<DT, BM, BN, BK, 2>},                         \
-    {DT, BM, BN, BK, 3, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 3 <= kLdsBytes) ? 3 : 2>}, \
-    {DT, BM, BN, BK, 4, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 4 <= kLdsBytes) ? 4 : 2>}, \
-    {DT, BM, BN, BK, 5, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 5 <= kLdsBytes) ? 5 : 2>}
+#define TSG_SLOTS(DT, BM, BN, BK, WGN)                                                                     \
+    {DT, BM, BN, BK, 2, 2 * WGN, launch<DT, BM, BN, BK, 2, WGN>},                                          \
+    {DT, BM, BN, BK, 3, 2 * WGN, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 3 <= kLdsBytes) ? 3 : 2, WGN>}, \
+    {DT, BM, BN, BK, 4, 2 * WGN, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 4 <= kLdsBytes) ? 4 : 2, WGN>}, \
+    {DT, BM, BN, BK, 5, 2 * WGN, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 5 <= kLdsBytes) ? 5 : 2, WGN>}
+#define TSG_TILE(DT, BM, BN, BK) TSG_SLOTS(DT, BM, BN, BK, 2), TSG_SLOTS(DT, BM, BN, BK, 4)
 
 const KernelEntry kKernels[] = {
     TSG_TILE(1, 128, 128, 32), TSG_TILE(1, 128, 128, 64), TSG_TILE(1, 256, 256, 32), TSG_TILE(1, 256, 256, 64),
     TSG_TILE(2, 128, 128, 32), TSG_TILE(2, 128, 128, 64), TSG_TILE(2, 256, 256, 32), TSG_TILE(2, 256, 256, 64),
 };
 
-const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots) {
+// Default wavefronts per workgroup for a tile shape (measured on MI355X).
+int default_waves(int bm, int bn, int bk) {
+    (void)bm; (void)bn; (void)bk;
+    return 4;
+}
+
+const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots, int waves) {
     for (const KernelEntry& e : kKernels)
-        if (e.dt == dt && e.bm == bm && e.bn == bn && e.bk == bk && e.slots == slots) return &e;
+        if (e.dt == dt && e.bm == bm && e.bn == bn && e.bk == bk && e.slots == slots && e.waves == waves) return &e;
     return nullptr;
 }
 
@@ -199,7 +206,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     if (slots < 2) { fail(TSGEMM_EUNSUPPORTED, "two %d-byte stages do not fit in LDS", stage); return nullptr; }
     const int64_t mb = (M + block_M - 1) / block_M, nb = (N + block_N - 1) / block_N;
     if (mb * nb >= lim) { fail(TSGEMM_EUNSUPPORTED, "tile count must be below 2^31"); return nullptr; }
-    const KernelEntry* k = find_kernel(dtype, block_M, block_N, block_K, slots);
+    const KernelEntry* k = find_kernel(dtype, block_M, block_N, block_K, slots, default_waves(block_M, block_N, block_K));
     if (!k) { fail(TSGEMM_EUNSUPPORTED, "no kernel for this configuration"); return nullptr; }
     tsgemm_plan* p = new (std::nothrow) tsgemm_plan;
     if (!p) { fail(TSGEMM_ENOMEM, "out of host memory"); return nullptr; }
@@ -216,6 +223,17 @@ int tsgemm_set_num_workgroups(tsgemm_plan* p, int num_workgroups) {
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (num_workgroups < 0) return fail(TSGEMM_EINVAL, "num_workgroups must be >= 0");
     p->P = num_workgroups;
+    return TSGEMM_OK;
+}
+
+int tsgemm_set_waves(tsgemm_plan* p, int waves) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (waves == 0) waves = default_waves(p->bm, p->bn, p->bk);
+    if (waves != 4 && waves != 8) return fail(TSGEMM_EINVAL, "waves must be 0, 4 or 8, got %d", waves);
+    const KernelEntry* k = find_kernel(p->dtype, p->bm, p->bn, p->bk, p->slots, waves);
+    if (!k) return fail(TSGEMM_EUNSUPPORTED, "no %d-wave kernel for this configuration", waves);
+    p->kernel = k;
     return TSGEMM_OK;
 }
 
@@ -268,7 +286,7 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
     info->k_blocks = p->k_blocks; info->num_tiles = p->tiles;
     info->num_workgroups = p->P;  // explicit P only; default resolves at run time
     info->waves = p->P ? (int32_t)((p->tiles + p->P - 1) / p->P) : 0;
-    info->threads_per_workgroup = tsg::kThreads;
+    info->threads_per_workgroup = 64 * p->kernel->waves;
     info->xcd_remap = p->xcd_remap;
     return TSGEMM_OK;
 }

@@ -59,7 +59,16 @@ enum { DT_FP16 = 1, DT_BF16 = 2 };
 #define TSG_DMA_SPACING 3
 #endif
 constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA issues
-constexpr int kThreads = 256;
+#ifndef TSG_GAP
+#define TSG_GAP 4
+#endif
+constexpr int kGap = TSG_GAP;  // MFMAs between the last read of a fragment set and its refill
+
+// Idle issue slots covering an in-flight MFMA's operand fetch and result write
+// (MFMAs here are asm, so the compiler inserts no wait states for them).
+__device__ __forceinline__ void gap_nops() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+__device__ __forceinline__ void store_gap() { asm volatile("s_nop 7\n\ts_nop 7" ::: "memory"); }
+constexpr int kMaxThreads = 512;
 constexpr uint32_t kRawBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
 
 struct GemmArgs {
@@ -123,9 +132,11 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int DT, int BM, int BN, int BK, int L>
+template <int DT, int BM, int BN, int BK, int L, int WGN>
 struct GemmTraits {
-    static constexpr int WM = BM / 2, WN = BN / 2;          // wave sub-tile
+    static constexpr int NW = 2 * WGN;                      // waves: 2 along M x WGN along N
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int WM = BM / 2, WN = BN / WGN;        // wave sub-tile
     static constexpr int FM = WM / 16, FN = WN / 16;        // 16x16 blocks per wave
     static constexpr int KS = BK / 32;                      // MFMA k-steps per slab
     static constexpr int CA = BK / 8;                       // 16-byte chunks per A row
@@ -134,12 +145,14 @@ struct GemmTraits {
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS = STAGE * L;
-    static constexpr int NA = A_BYTES / (1024 * 4);         // DMA instructions per wave, A
-    static constexpr int NB = B_BYTES / (1024 * 4);         // DMA instructions per wave, B
+    static constexpr int NA = A_BYTES / (1024 * NW);        // DMA instructions per wave, A
+    static constexpr int NB = B_BYTES / (1024 * NW);        // DMA instructions per wave, B
     static constexpr int NL = NA + NB;
     static_assert(BK == 32 || BK == 64, "block_K");
     static_assert(FN % 2 == 0 && FM >= 1, "wave tile");
-    static_assert(NA >= 1 && NB >= 1, "slab too small for 4 waves");
+    static_assert(NA >= 1 && NB >= 1 && NA * 1024 * NW == A_BYTES && NB * 1024 * NW == B_BYTES,
+                  "slab must split into whole 1 KiB DMAs per wave");
+    static_assert(WGN == 2 || WGN == 4, "wave grid");
     static_assert(LDS <= 160 * 1024, "LDS");
     static_assert(CB >= 16, "B swizzle needs 16 chunks per row");
 };
@@ -170,7 +183,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // cannot tell the stage being filled from the stage being read); the kernel
 // waits on vmcnt itself before the barrier that publishes a stage.
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+    // s_nop: one wait state between the M0 write the compiler emits and its use
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                 : "memory");
 }
 
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
@@ -184,16 +199,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
     return r;
 }
 
-template <int DT, int BM, int BN, int BK, int L>
-__global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
-    using T = GemmTraits<DT, BM, BN, BK, L>;
+template <int DT, int BM, int BN, int BK, int L, int WGN>
+__global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) {
+    using T = GemmTraits<DT, BM, BN, BK, L, WGN>;
     constexpr int FM = T::FM, FN = T::FN, KS = T::KS, NA = T::NA, NB = T::NB, NL = T::NL;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
     const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem);
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t wr = wave >> 1, wc = wave & 1u;  // wave row / column in the 2x2 grid
+    const uint32_t wr = wave / WGN, wc = wave % WGN;  // wave row / column in the 2 x WGN grid
     const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K;
     const uint32_t k_blocks = args.k_blocks;
     const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
@@ -288,14 +303,14 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
             dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u, voff[q], rs_b);
     };
 
-    // ---- fragments: A single-buffered (block fm is refilled right after its
-    // last MFMA), B in two sets (every B block is used until the k-step ends) ----
+    // ---- fragments: two register sets for A and B, the one the MFMAs of this
+    // k-step read and the one the next k-step's LDS reads fill ----
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i16x8 fa[FM];
+    i16x8 fa[2][FM];
     i16x4 fb[2][FN][2];
 
     // LDS reads of one k-step: A block fm, and B halves (fn, h) into set SET.
@@ -308,9 +323,9 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) rb[fn] = lds_base + st + b_off[fn] + KSN * 32 * (BN * 2);
     };
-    auto read_a = [&](auto fm_c) __attribute__((always_inline)) {
-        constexpr int fm = decltype(fm_c)::value;
-        fa[fm] = __builtin_bit_cast(i16x8, *(const __attribute__((address_space(3))) u32x4*)(
+    auto read_a = [&](auto set_c, auto fm_c) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_c)::value, fm = decltype(fm_c)::value;
+        fa[SET][fm] = __builtin_bit_cast(i16x8, *(const __attribute__((address_space(3))) u32x4*)(
                                                (__attribute__((address_space(3))) uint8_t*)(uintptr_t)ra + fm * 16 * (BK * 2)));
     };
     auto read_b = [&](auto set_c, auto r_c) __attribute__((always_inline)) {
@@ -319,22 +334,32 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
         fb[SET][fn][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4*)((__attribute__((address_space(3))) uint8_t*)(uintptr_t)rb[fn] + h * 4 * (BN * 2)));
     };
-    constexpr int RB = 2 * FN;
+    // read op r of a k-step in consumption order: A block 0, the B halves,
+    // then A blocks 1..FM-1
+    constexpr int R = FM + 2 * FN;
+    auto read_op = [&](auto set_c, auto r_c) __attribute__((always_inline)) {
+        constexpr int r = decltype(r_c)::value;
+        if constexpr (r == 0 || r > 2 * FN)
+            read_a(set_c, std::integral_constant<int, (r == 0 ? 0 : r - 2 * FN)>{});
+        else
+            read_b(set_c, std::integral_constant<int, r - 1>{});
+    };
     auto read_all = [&](auto set_c, auto ks_c, uint32_t st) __attribute__((always_inline)) {
         set_addr(ks_c, st);
-        static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) { read_a(fm_c); });
-        static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(set_c, r_c); });
+        static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, r_c); });
     };
 
-    // One 32-deep k-step: FM*FN MFMAs (fm-major) from A and B set CUR,
+    // One 32-deep k-step: FM*FN MFMAs (fm-major) from register set CUR,
     // accumulating into tiles that the epilogue left at zero (the k == 0
-    // clear), with the memory operations for what follows between them: A
-    // block fm is refilled right after its last use; the DMA and the B reads
-    // into set NXT are spread over the remaining steps.  LAST (the slab's last
-    // k-step) first waits for the next slab and passes the workgroup barrier,
-    // then issues the DMA of slab phase+L into the stage just consumed and reads
-    // the next slab's first k-step; otherwise it reads k-step KSN of the
-    // current stage.  SAME (an odd tail slab) refills B set CUR after its MFMAs.
+    // clear), with the memory operations for what follows between them: the
+    // DMA (LAST only) and the reads of the next k-step into set NXT.  No read
+    // into a set starts within kGap MFMAs of the last MFMA that read it: an
+    // MFMA may still be fetching its operands, and a second wave on the SIMD
+    // can delay it.  LAST (the slab's last k-step) first waits for the next
+    // slab and passes the workgroup barrier, then issues the DMA of slab
+    // phase+L into the stage just consumed and reads the next slab's first
+    // k-step; otherwise it reads k-step KSN of the current stage.  SAME (an
+    // odd tail slab) refills set CUR after its MFMAs.
     auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr bool SAME = decltype(same_c)::value;
@@ -342,41 +367,42 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
         constexpr bool LAST = decltype(last_c)::value;
         if constexpr (LAST) next_slab();  // scalar only; the DMA itself waits for the barrier
         constexpr int NSTEP = FM * FN;
-        constexpr int S0 = LAST ? 2 : 0;                  // MFMAs issued before the barrier
+        constexpr int S0 = LAST ? 2 : 0;                   // MFMAs issued before the barrier
+        constexpr int START = S0 > kGap ? S0 : kGap;       // first step with memory operations
+        constexpr int AVAIL = NSTEP - START - 1;
+        static_assert(AVAIL >= 2, "k-step too short for its memory operations");
         constexpr int D = LAST ? NL : 0;
-        constexpr int AVAIL = NSTEP - S0 > 4 ? NSTEP - S0 - 2 : NSTEP - S0;
         // DMA issues are spaced DS MFMAs apart: a burst of them right after the
-        // barrier (4 waves at once) would overflow the texture unit's queue and
-        // stall instruction issue, MFMAs included
+        // barrier would overflow the texture unit's queue and stall issue
         constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
-        constexpr int QB = SAME ? 0 : RB;                 // B reads, spread evenly
-        constexpr int PER = QB ? (QB + AVAIL - 1) / AVAIL : 0;
-        static_assert(FN - 1 >= S0, "A refills must follow the barrier");
+        constexpr int QR = SAME ? 0 : R;                   // reads, spread evenly
+        constexpr int PER = QR ? (QR + AVAIL - 1) / AVAIL : 0;
         if constexpr (!LAST) set_addr(ksn_c, read_st);
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / FN, fn = s % FN;
             const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            mfma16x16x32<DT>(acc[fm][fn], bv, fa[fm]);
+            mfma16x16x32<DT>(acc[fm][fn], bv, fa[CUR][fm]);
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
                 set_addr(ksn_c, read_st);
             }
-            if constexpr (s >= S0) {
-                constexpr int i = s - S0;
+            if constexpr (s >= START) {
+                constexpr int i = s - START;
                 if constexpr (D && i % DS == 0 && i / DS < D) dma_op(std::integral_constant<int, i / DS>{});
                 constexpr int q0 = i * PER;
-                constexpr int q1 = q0 + PER < QB ? q0 + PER : QB;
+                constexpr int q1 = q0 + PER < QR ? q0 + PER : QR;
                 static_for<q0, q1>([&](auto q_c) __attribute__((always_inline)) {
-                    read_b(std::integral_constant<int, NXT>{}, q_c);
+                    read_op(std::integral_constant<int, NXT>{}, q_c);
                 });
             }
-            if constexpr (fn == FN - 1) read_a(std::integral_constant<int, fm>{});
             __builtin_amdgcn_sched_barrier(0);
         });
-        if constexpr (SAME)
-            static_for<0, RB>([&](auto r_c) __attribute__((always_inline)) { read_b(cur_c, r_c); });
+        if constexpr (SAME) {
+            gap_nops();
+            static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(cur_c, r_c); });
+        }
     };
 
     using I0 = std::integral_constant<int, 0>;
@@ -395,10 +421,12 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
     const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
     const uint32_t lane_off = (row0 * N + col0) * 2u;
     auto epilogue = [&]() __attribute__((always_inline)) {
+        gap_nops();  // the tile's last MFMAs have written their accumulators
         const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
         if (args.trace != nullptr && threadIdx.x == 0) {
             int32_t* row = args.trace + 4 * ((size_t)wid * args.max_iters + sched.iter);
             *(int4*)row = make_int4((int)wid, (int)sched.iter, (int)m_idx, (int)n_idx);
+            store_gap();
         }
         const int64_t m0 = (int64_t)m_idx * BM, n0 = (int64_t)n_idx * BN;
         const uint32_t rows_left = (uint32_t)((args.M - m0) < BM ? (args.M - m0) : BM);
@@ -417,6 +445,10 @@ __global__ __launch_bounds__(kThreads, 1) void tsgemm_kernel(GemmArgs args) {
                 const bool ok = row_ok && col0 + 32u * t < cols_left;
                 __builtin_amdgcn_raw_buffer_store_b128(v, rc, (ok ? lane_off : 0x80000000u) + t * 64,
                                                        fm * 16 * N * 2, 0);
+                // The store may read its data registers after it issues (a second
+                // wave's memory traffic can hold it back); keep them intact for a
+                // while before the next conversion overwrites them.
+                store_gap();
                 acc[fm][2 * t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 acc[fm][2 * t + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 __builtin_amdgcn_sched_barrier(0);

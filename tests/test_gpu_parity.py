@@ -50,9 +50,9 @@ def _run(plan, A, B, dtype, guard=0, fill=float("nan")):
     return C.cpu(), buf[M * N:].cpu()
 
 
-def _full_check(M, N, K, dtype, dist, seed, bm, bn, bk, gs, S, P=0, xcd=True):
+def _full_check(M, N, K, dtype, dist, seed, bm, bn, bk, gs, S, P=0, xcd=True, waves=0):
     A, B = make_inputs(M, N, K, dtype, dist, seed)
-    plan = tsg.Plan(M, N, K, dtype, bm, bn, bk, gs, S, num_workgroups=P, xcd_remap=xcd)
+    plan = tsg.Plan(M, N, K, dtype, bm, bn, bk, gs, S, num_workgroups=P, xcd_remap=xcd, waves=waves)
     C, guard = _run(plan, A, B, dtype, guard=64)
     assert torch.isnan(guard.float()).all(), "write past the end of C"
     ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[dtype])
@@ -71,16 +71,17 @@ def test_small_workloads_full_compare(cfg):
 TILES = [(128, 128, 32), (128, 128, 64), (256, 256, 32), (256, 256, 64)]
 
 
+@pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("S", [2, 3, 4, 5])
-def test_ragged_shapes_every_kernel(dtype, tile, S):
+def test_ragged_shapes_every_kernel(dtype, tile, S, waves):
     bm, bn, bk = tile
     # several tiles with ragged row and column tails; K gives an odd slab count
     M, N, K = 2 * bm + bm // 2 + 8, 2 * bn + 24, 7 * bk
-    print(f"[case] ragged {dtype} {tile} S={S} {M}x{N}x{K}", flush=True)
+    print(f"[case] ragged {dtype} {tile} S={S} waves={waves} {M}x{N}x{K}", flush=True)
     dist = "uniform" if dtype == "fp16" else "normal_sqrtk"
-    _full_check(M, N, K, dtype, dist, 100 + S, bm, bn, bk, 2, S, P=3)
+    _full_check(M, N, K, dtype, dist, 100 + S, bm, bn, bk, 2, S, P=3, waves=waves)
 
 
 @pytest.mark.parametrize("P", [1, 2, 5, 8, 64, 300])
