@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
 #define TSG_HD __host__ __device__ __forceinline__
 #else
 #define TSG_HD inline

@@ -69,6 +69,16 @@ const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots, int wa
     return nullptr;
 }
 
+// LDS ring depth in block_K slabs: min(num_stages, LDS / stage, kMaxSlots);
+// 0 when two stages do not fit.
+int ring_slots(int bm, int bn, int bk, int stages) {
+    const int stage = (bm * bk + bk * bn) * 2;
+    int slots = kLdsBytes / stage;
+    if (slots > stages) slots = stages;
+    if (slots > kMaxSlots) slots = kMaxSlots;
+    return slots >= 2 ? slots : 0;
+}
+
 bool tile_supported(int bm, int bn, int bk) {
     return (bm == 128 && bn == 128 && (bk == 32 || bk == 64)) ||
            (bm == 256 && bn == 256 && (bk == 32 || bk == 64));
@@ -200,9 +210,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
         return nullptr;
     }
     const int stage = (block_M * block_K + block_K * block_N) * 2;
-    int slots = kLdsBytes / stage;
-    if (slots > num_stages) slots = num_stages;
-    if (slots > kMaxSlots) slots = kMaxSlots;
+    const int slots = ring_slots(block_M, block_N, block_K, num_stages);
     if (slots < 2) { fail(TSGEMM_EUNSUPPORTED, "two %d-byte stages do not fit in LDS", stage); return nullptr; }
     const int64_t mb = (M + block_M - 1) / block_M, nb = (N + block_N - 1) / block_N;
     if (mb * nb >= lim) { fail(TSGEMM_EUNSUPPORTED, "tile count must be below 2^31"); return nullptr; }

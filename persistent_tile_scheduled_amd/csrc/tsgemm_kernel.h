@@ -32,102 +32,10 @@
 //     along N and the epilogue writes 16 contiguous bytes per lane.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
-
 #include "tile_scheduler.h"
+#include "tsgemm_device.h"
 
 namespace tsg {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-enum { DT_FP16 = 1, DT_BF16 = 2 };
-#ifndef TSG_DMA_SPACING
-#define TSG_DMA_SPACING 3
-#endif
-constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA issues
-#ifndef TSG_GAP
-#define TSG_GAP 4
-#endif
-constexpr int kGap = TSG_GAP;  // MFMAs between the last read of a fragment set and its refill
-
-// Idle issue slots covering an in-flight MFMA's operand fetch and result write
-// (MFMAs here are asm, so the compiler inserts no wait states for them).
-__device__ __forceinline__ void gap_nops() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-__device__ __forceinline__ void store_gap() { asm volatile("s_nop 7\n\ts_nop 7" ::: "memory"); }
-constexpr int kMaxThreads = 512;
-constexpr uint32_t kRawBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
-
-struct GemmArgs {
-    const uint16_t* A;
-    const uint16_t* B;
-    uint16_t* C;
-    int32_t* trace;  // optional (worker, iter, m, n) per processed tile
-    int64_t M, N, K;
-    uint32_t m_blocks, n_blocks, k_blocks, group;
-    uint32_t P, max_iters, num_xcd;
-};
-
-// ---------------------------------------------------------------------------
-// small device helpers
-// ---------------------------------------------------------------------------
-// acc += a * b on the 16x16x32 matrix core.  Written as asm with the
-// accumulator constrained to AGPRs: each 16x16 fp32 tile stays in one fixed
-// AGPR quad for the whole kernel and the VGPRs are left to the fragments.
-template <int DT>
-__device__ __forceinline__ void mfma16x16x32(f32x4& acc, i16x8 a, i16x8 b) {
-    if constexpr (DT == DT_FP16)
-        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-    else
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Two fp32 accumulators (held in AGPRs) -> one dword of two 16-bit values
-// (low half = a), round to nearest even.  The AGPR reads sit inside the asm so
-// they happen at the store that needs them rather than all up front.
-template <int DT>
-__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
-    uint32_t r, t;
-    if constexpr (DT == DT_FP16)
-        asm volatile("v_accvgpr_read_b32 %0, %2\n\tv_accvgpr_read_b32 %1, %3\n\tv_cvt_pk_f16_f32 %0, %0, %1"
-                     : "=&v"(r), "=&v"(t) : "a"(a), "a"(b));
-    else
-        asm volatile("v_accvgpr_read_b32 %0, %2\n\tv_accvgpr_read_b32 %1, %3\n\tv_cvt_pk_bf16_f32 %0, %0, %1"
-                     : "=&v"(r), "=&v"(t) : "a"(a), "a"(b));
-    return r;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             (int)kRawBufferFlags);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// All LDS reads of this wave done, then workgroup barrier.  The asm is a
-// compiler memory barrier too, so no LDS access moves across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // ---------------------------------------------------------------------------
 // the kernel
@@ -157,47 +65,6 @@ struct GemmTraits {
     static_assert(CB >= 16, "B swizzle needs 16 chunks per row");
 };
 
-// Swizzled 16-byte chunk slot of logical chunk c in LDS row r.
-template <int CA>
-__device__ __forceinline__ uint32_t swz_a(uint32_t r) {
-    // 8 consecutive rows at one logical chunk land on 8 distinct bank groups
-    return CA == 8 ? (r & 7u) : ((r >> 1) & 3u);
-}
-__device__ __forceinline__ uint32_t swz_b(uint32_t kr) {
-    // the 4 rows of one transpose read, and the two row octets a wave reads
-    // together, land on distinct bank groups
-    const uint32_t s = (kr & 1u) | ((kr & 2u) << 1);  // 0,1,4,5 for kr%4 = 0..3
-    return s | (((kr >> 3) & 1u) << 3);
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-// One 16-byte-per-lane DMA from a buffer into LDS.  Issued as inline asm so
-// the compiler does not treat every later LDS read as dependent on it (it
-// cannot tell the stage being filled from the stage being read); the kernel
-// waits on vmcnt itself before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-    // s_nop: one wait state between the M0 write the compiler emits and its use
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-                 : "memory");
-}
-
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    // all four words are wave-uniform; readfirstlane keeps them in SGPRs
-    i32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));  // stride 0
-    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-    r.w = (int)kRawBufferFlags;
-    return r;
-}
 
 template <int DT, int BM, int BN, int BK, int L, int WGN>
 __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) {

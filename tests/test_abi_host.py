@@ -85,6 +85,23 @@ def test_plan_info_matches_workload(name):
     assert inf["stage_bytes"] == stage
     assert inf["lds_slots"] == min(w.num_stages, 160 * 1024 // stage, 5)
     assert inf["lds_bytes"] <= 160 * 1024 and inf["lds_slots"] >= 2
+    assert inf["threads_per_workgroup"] == 256
+
+
+@pytest.mark.parametrize("tile", [(128, 128, 32), (128, 128, 64), (256, 256, 32), (256, 256, 64)])
+def test_set_waves(tile):
+    """8 waves (2x4 grid, two per SIMD) run the same LDS ring; bad counts are refused."""
+    bm, bn, bk = tile
+    lib = tsg.load()
+    plan = tsg.Plan(1024, 1024, 512, "bf16", bm, bn, bk, 4, 3)
+    base = plan.info()
+    assert lib.tsgemm_set_waves(plan._h, 8) == 0
+    inf = plan.info()
+    assert inf["threads_per_workgroup"] == 512
+    assert (inf["lds_slots"], inf["lds_bytes"]) == (base["lds_slots"], base["lds_bytes"])
+    assert lib.tsgemm_set_waves(plan._h, 6) == tsg.EINVAL and "waves" in tsg.last_error()
+    assert plan.info()["threads_per_workgroup"] == 512  # a refused call leaves the plan as it was
+    assert lib.tsgemm_set_waves(plan._h, 0) == 0 and plan.info()["threads_per_workgroup"] == 256
 
 
 def test_sm90_stage_arithmetic():

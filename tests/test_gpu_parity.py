@@ -90,6 +90,20 @@ def test_worker_counts(P):
     _full_check(640, 768, 384, "bf16", "normal_sqrtk", 200 + P, 128, 128, 64, 3, 2, P=P)
 
 
+@pytest.mark.parametrize("P", [1, 2, 5, 300])
+def test_worker_counts_eight_waves(P):
+    print(f"[case] 8 waves P={P}", flush=True)
+    _full_check(640, 776, 384, "bf16", "normal_sqrtk", 210 + P, 256, 256, 64, 3, 3, P=P, waves=8)
+
+
+def test_eight_waves_tiny_and_deep():
+    print("[case] 8 waves tiny", flush=True)
+    _full_check(1, 16, 64, "bf16", "uniform", 311, 256, 256, 32, 1, 4, waves=8)
+    _full_check(130, 264, 64, "fp16", "uniform", 312, 256, 256, 64, 2, 2, waves=8)
+    # many tiles per worker and a long K: the loader crosses tile boundaries often
+    _full_check(1000, 1032, 1536, "fp16", "uniform", 313, 256, 256, 64, 1, 3, P=3, waves=8)
+
+
 def test_xcd_remap_off_matches():
     print("[case] xcd off", flush=True)
     _full_check(1024, 1024, 256, "fp16", "uniform", 300, 128, 128, 32, 4, 3, P=0, xcd=False)
@@ -152,9 +166,9 @@ def test_output_rounding_is_nearest_even(dtype):
 
 
 # ---------------------------------------------------------------- schedule
-def _plan_for(w, P=None):
+def _plan_for(w, waves=0):
     return tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
-                    w.num_stages, num_workgroups=w.num_workgroups if P is None else P)
+                    w.num_stages, num_workgroups=w.num_workgroups, waves=waves)
 
 
 @pytest.mark.parametrize("cfg", sorted(WORKLOADS))
@@ -168,12 +182,13 @@ def test_schedule_dump_bit_exact(cfg):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("cfg", ["cfg1_512_fp16", "cfg2_1024_fp16", "cfg4p_16000x4000x4096_fp16"])
-def test_gemm_kernel_trace_matches_oracle(cfg):
+@pytest.mark.parametrize("cfg,waves", [("cfg1_512_fp16", 0), ("cfg2_1024_fp16", 0),
+                                       ("cfg4p_16000x4000x4096_fp16", 4), ("cfg4p_16000x4000x4096_fp16", 8)])
+def test_gemm_kernel_trace_matches_oracle(cfg, waves):
     """The GEMM kernel's own record of the tiles it processed."""
     w = WORKLOADS[cfg]
-    print(f"[case] trace {cfg}", flush=True)
-    plan = _plan_for(w)
+    print(f"[case] trace {cfg} waves={waves}", flush=True)
+    plan = _plan_for(w, waves)
     P = plan.num_workgroups
     T = plan.num_tiles
     iters = -(-T // P)
@@ -190,9 +205,9 @@ def test_gemm_kernel_trace_matches_oracle(cfg):
 
 
 # ---------------------------------------------------------------- full size, sampled
-def _sampled_check(w, n_samples=6000, seed=9):
+def _sampled_check(w, n_samples=6000, seed=9, waves=0):
     A, B = workload_inputs(w)
-    plan = _plan_for(w)
+    plan = _plan_for(w, waves)
     guard = 4096
     C, g = _run(plan, A, B, w.dtype, guard=guard)
     assert torch.isnan(g.float()).all(), "write past the end of C"
@@ -215,9 +230,10 @@ def _sampled_check(w, n_samples=6000, seed=9):
 
 @pytest.mark.parametrize("cfg", ["cfg3_8192_bf16", "cfg4_16384x4096x4096_fp16",
                                  "cfg4p_16000x4000x4096_fp16", "cfg5_2048x2048x32768_bf16"])
-def test_full_size_sampled(cfg):
-    print(f"[case] full {cfg}", flush=True)
-    _sampled_check(WORKLOADS[cfg])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_full_size_sampled(cfg, waves):
+    print(f"[case] full {cfg} waves={waves}", flush=True)
+    _sampled_check(WORKLOADS[cfg], waves=waves)
 
 
 def test_full_tile_of_8192_exact_compare():
