@@ -24,19 +24,38 @@ Readings taken where the pages are silent:
   * The number of workers is the number of persistent workgroups (the page uses
     the SM count with one CTA per worker).
 
+Two scheduler options named in the PR overview on the same page
+(PersistentTileScheduler's cluster_size and column_major), read as follows:
+  * cluster_size = cs (the 2-CTA variant gemm_persistent_2cta): workgroup
+    ``wid`` belongs to cluster ``wid // cs`` with rank ``cta = wid % cs``; the
+    scheduler runs over ``P // cs`` clusters (init(block_id // cluster_size))
+    on a grid of ``ceil(m_blocks / cs)`` cluster rows by n_blocks, and the
+    workgroup takes row block ``bx = m_idx * cs + cta``, column ``n_idx``.  When
+    m_blocks is not a multiple of cs the tail cluster's bx can pass the last row
+    block; the review on the page asks for a ``bx < m_blocks`` guard, read here
+    as: that workgroup skips the iteration (no tile, the wave index still
+    advances).  P must be a multiple of cs.
+  * column_major: the page gives only "axis fast/slow selection".  Read as the
+    transpose of the default decode: groups of group_size row blocks, and inside
+    a group the tiles run column by column (n slow, m fast).
+
 Rows are (worker, iter, m_idx, n_idx) sorted by (worker, iter).
 """
 
 from __future__ import annotations
 
 
-def coord(tile_id: int, m_blocks: int, n_blocks: int, group_size: int) -> tuple[int, int]:
+def coord(tile_id: int, m_blocks: int, n_blocks: int, group_size: int,
+          column_major: bool = False) -> tuple[int, int]:
     """Stateless decode of one linear tile id into (m_idx, n_idx).
 
     Column groups of ``group_size`` n-blocks are walked in order; inside a group
     the tiles are laid out row after row (m slow, n fast), each row being as
-    wide as the group.
+    wide as the group.  ``column_major`` swaps the roles of m and n.
     """
+    if column_major:
+        n, m = coord(tile_id, n_blocks, m_blocks, group_size)
+        return m, n
     per_group = group_size * m_blocks
     group = tile_id // per_group
     first_col = group * group_size
@@ -45,46 +64,76 @@ def coord(tile_id: int, m_blocks: int, n_blocks: int, group_size: int) -> tuple[
     return r // width, first_col + r % width
 
 
-def schedule_closed_form(num_workers: int, m_blocks: int, n_blocks: int,
-                         group_size: int) -> list[tuple[int, int, int, int]]:
+def _cluster_grid(num_workers: int, m_blocks: int, cluster_size: int):
+    if cluster_size < 1 or num_workers % cluster_size:
+        raise ValueError("the number of workers must be a multiple of cluster_size")
+    return num_workers // cluster_size, -(-m_blocks // cluster_size)
+
+
+def schedule_closed_form(num_workers: int, m_blocks: int, n_blocks: int, group_size: int,
+                         column_major: bool = False, cluster_size: int = 1
+                         ) -> list[tuple[int, int, int, int]]:
     """Worker-major enumeration driven by the wave clock.
 
-    For each worker: start at wave 0, visit tile ``num_workers * w + worker``
-    while it is below the tile count, then advance the wave index.
+    For each worker: start at wave 0, visit cluster tile ``clusters * w +
+    cluster`` while it is below the cluster-tile count, take row block
+    ``m * cs + cta`` of it when that block exists, then advance the wave index.
     """
-    tiles = m_blocks * n_blocks
+    clusters, m_cl = _cluster_grid(num_workers, m_blocks, cluster_size)
+    tiles = m_cl * n_blocks
     rows = []
     for worker in range(num_workers):
+        cluster, cta = divmod(worker, cluster_size)
         w = 0
-        while num_workers * w + worker < tiles:
-            m, n = coord(num_workers * w + worker, m_blocks, n_blocks, group_size)
-            rows.append((worker, w, m, n))
+        while clusters * w + cluster < tiles:
+            m, n = coord(clusters * w + cluster, m_cl, n_blocks, group_size, column_major)
+            bx = m * cluster_size + cta
+            if bx < m_blocks:
+                rows.append((worker, w, bx, n))
             w += 1
     return rows
 
 
-def schedule_by_walk(num_workers: int, m_blocks: int, n_blocks: int,
-                     group_size: int) -> list[tuple[int, int, int, int]]:
+def schedule_by_walk(num_workers: int, m_blocks: int, n_blocks: int, group_size: int,
+                     column_major: bool = False, cluster_size: int = 1
+                     ) -> list[tuple[int, int, int, int]]:
     """Second, independent construction of the same schedule.
 
-    First write down the global visiting order by walking the column groups,
-    then the rows inside a group, then the columns of the group; then deal the
-    ordered list round-robin: item i goes to worker i % P at wave i // P.
+    First write down the global visiting order of cluster tiles by walking the
+    groups, then the rows (columns, if column-major) inside a group, then the
+    other axis within the group; deal the ordered list round-robin to the
+    clusters (item i to cluster i % C at wave i // C); finally split every
+    cluster tile into its cs row blocks, one per rank, dropping blocks past the
+    last row.
     """
+    clusters, m_cl = _cluster_grid(num_workers, m_blocks, cluster_size)
     order = []
-    for first_col in range(0, n_blocks, group_size):
-        cols = list(range(first_col, min(first_col + group_size, n_blocks)))
-        for m in range(m_blocks):
-            for n in cols:
-                order.append((m, n))
-    dealt = [(i % num_workers, i // num_workers, m, n) for i, (m, n) in enumerate(order)]
+    if not column_major:
+        for first_col in range(0, n_blocks, group_size):
+            cols = list(range(first_col, min(first_col + group_size, n_blocks)))
+            for m in range(m_cl):
+                for n in cols:
+                    order.append((m, n))
+    else:
+        for first_row in range(0, m_cl, group_size):
+            rws = list(range(first_row, min(first_row + group_size, m_cl)))
+            for n in range(n_blocks):
+                for m in rws:
+                    order.append((m, n))
+    dealt = []
+    for i, (m, n) in enumerate(order):
+        cluster, w = i % clusters, i // clusters
+        for cta in range(cluster_size):
+            if m * cluster_size + cta < m_blocks:
+                dealt.append((cluster * cluster_size + cta, w, m * cluster_size + cta, n))
     return sorted(dealt)
 
 
-def schedule(num_workers: int, m_blocks: int, n_blocks: int, group_size: int):
+def schedule(num_workers: int, m_blocks: int, n_blocks: int, group_size: int,
+             column_major: bool = False, cluster_size: int = 1):
     """The reference schedule; both constructions must agree."""
-    a = schedule_closed_form(num_workers, m_blocks, n_blocks, group_size)
-    b = schedule_by_walk(num_workers, m_blocks, n_blocks, group_size)
+    a = schedule_closed_form(num_workers, m_blocks, n_blocks, group_size, column_major, cluster_size)
+    b = schedule_by_walk(num_workers, m_blocks, n_blocks, group_size, column_major, cluster_size)
     if a != b:
         raise AssertionError("schedule constructions disagree")
     return a
