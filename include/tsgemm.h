@@ -64,9 +64,12 @@ typedef struct tsgemm_info {
     int32_t lds_bytes;       /* lds_slots * stage_bytes                              */
     int64_t m_blocks, n_blocks, k_blocks, num_tiles;
     int32_t num_workgroups;  /* P; 0 while unresolved (default P before a device is seen) */
-    int32_t waves;           /* ceil(num_tiles / P); 0 while P is unresolved         */
+    int32_t waves;           /* waves of the busiest workgroup, ceil(ceil(m_blocks/cs) * n_blocks
+                                / (P/cs)) for cluster size cs; 0 while P is unresolved        */
     int32_t threads_per_workgroup;
     int32_t xcd_remap;       /* 1: workgroup -> worker id permuted so XCDs get compact tile blocks */
+    int32_t cluster_size;    /* tile scheduler: workgroups per cluster (1 = none)     */
+    int32_t column_major;    /* tile scheduler: 1 = transposed tile walk              */
 } tsgemm_info;
 
 /*
@@ -96,6 +99,18 @@ int tsgemm_set_num_workgroups(tsgemm_plan* plan, int num_workgroups);
  * restores the default for the tile shape.  Results are identical. */
 int tsgemm_set_waves(tsgemm_plan* plan, int waves);
 
+/* Tile scheduler options (page "[Feature] Introduce tile scheduler #2441",
+ * the PR overview of PersistentTileScheduler and its 2-CTA example):
+ *   cluster_size cs >= 1 (default 1): workgroup wid is rank wid % cs of
+ *     cluster wid / cs; clusters walk a ceil(m_blocks/cs) x n_blocks grid of
+ *     cluster tiles and each rank takes row block m*cs + rank, skipping the
+ *     wave when that block is past the last row (the review's bounds guard).
+ *     The number of workgroups must be a multiple of cs (checked at run).
+ *   column_major (default 0): 1 walks row groups of group_size blocks, m
+ *     fastest, instead of column groups with n fastest (the transpose).
+ * Results of tsgemm_run do not depend on either option. */
+int tsgemm_set_schedule(tsgemm_plan* plan, int column_major, int cluster_size);
+
 /* Enable (1, default) or disable (0) the XCD-aware workgroup -> worker id
  * permutation.  The schedule is defined on worker ids either way. */
 int tsgemm_set_xcd_remap(tsgemm_plan* plan, int enable);
@@ -108,8 +123,8 @@ int tsgemm_run(const tsgemm_plan* plan, const void* A, const void* B, void* C, v
 
 /* Same as tsgemm_run and additionally records every tile the GEMM kernel
  * processes: trace (DEVICE pointer, int32[4 * P * max_iters], max_iters =
- * ceil(num_tiles / P)) receives (worker, iter, m_idx, n_idx) at row
- * worker*max_iters + iter.  Diagnostic; rows not visited are left untouched. */
+ * tsgemm_info.waves for the run's P) receives (worker, iter, m_idx, n_idx) at
+ * row worker*max_iters + iter.  Diagnostic; rows not visited are left untouched. */
 int tsgemm_run_traced(const tsgemm_plan* plan, const void* A, const void* B, void* C,
                       void* stream, int32_t* trace);
 

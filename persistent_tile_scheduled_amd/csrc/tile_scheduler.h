@@ -27,38 +27,52 @@
 namespace tsg {
 
 struct TileScheduler {
-    uint32_t num_workers;  // P
-    uint32_t m_blocks, n_blocks, group, tiles;
-    uint32_t worker, iter, tile_id;
+    uint32_t num_workers;  // clusters: P / cluster
+    uint32_t m_blocks, n_blocks, group, cluster, col_major;
+    uint32_t m_cl;         // cluster rows: ceil(m_blocks / cluster)
+    uint32_t tiles;        // cluster tiles: m_cl * n_blocks
+    uint32_t rank, iter, tile_id;
     uint32_t m_idx, n_idx;
 
-    TSG_HD void setup(uint32_t P, uint32_t mb, uint32_t nb, uint32_t gs) {
-        num_workers = P;
+    // P workgroups in clusters of cs (P % cs == 0), decode column groups of gs
+    // blocks (cm = 0) or its transpose, row groups of gs blocks (cm = 1).
+    TSG_HD void setup(uint32_t P, uint32_t mb, uint32_t nb, uint32_t gs, uint32_t cs = 1, uint32_t cm = 0) {
+        cluster = cs;
+        col_major = cm;
+        num_workers = P / cs;
         m_blocks = mb;
         n_blocks = nb;
         group = gs;
-        tiles = mb * nb;
+        m_cl = (mb + cs - 1) / cs;
+        tiles = m_cl * nb;
     }
 
-    // Decode one linear tile id: column group g covers n blocks
-    // [g*group, g*group + width), width = group except a narrower last group;
-    // inside the group tiles run row by row.
+    // Decode one linear cluster-tile id on the m_cl x n_blocks grid.  Row-major:
+    // column group g covers n blocks [g*group, g*group + width), width = group
+    // except a narrower last group; inside the group tiles run row by row.
+    // Column-major: the same walk with the roles of rows and columns swapped.
     TSG_HD void coord(uint32_t t, uint32_t& m, uint32_t& n) const {
-        const uint32_t per_group = group * m_blocks;
+        const uint32_t rows = col_major ? n_blocks : m_cl;
+        const uint32_t cols = col_major ? m_cl : n_blocks;
+        const uint32_t per_group = group * rows;
         const uint32_t g = t / per_group;
         const uint32_t first = g * group;
-        const uint32_t rest = n_blocks - first;
+        const uint32_t rest = cols - first;
         const uint32_t width = rest < group ? rest : group;
         const uint32_t r = t - g * per_group;
         const uint32_t row = r / width;
-        m = row;
-        n = first + (r - row * width);
+        const uint32_t col = first + (r - row * width);
+        m = col_major ? col : row;
+        n = col_major ? row : col;
     }
 
+    // Workgroup wid is rank wid % cluster of cluster wid / cluster; the cluster
+    // visits tile ids cluster_id + num_workers * iter.
     TSG_HD void init(uint32_t wid) {
-        worker = wid;
+        const uint32_t c = wid / cluster;
+        rank = wid - c * cluster;
         iter = 0;
-        tile_id = wid;
+        tile_id = c;
         update();
     }
     TSG_HD bool valid() const { return tile_id < tiles; }
@@ -70,8 +84,21 @@ struct TileScheduler {
     TSG_HD uint32_t parity() const { return iter & 1u; }
 
   private:
+    // The workgroup takes row block m * cluster + rank of its cluster's tile;
+    // a rank whose row block is past the last one skips that wave.
     TSG_HD void update() {
-        if (valid()) coord(tile_id, m_idx, n_idx);
+        while (valid()) {
+            uint32_t m, n;
+            coord(tile_id, m, n);
+            const uint32_t bx = m * cluster + rank;
+            if (bx < m_blocks) {
+                m_idx = bx;
+                n_idx = n;
+                return;
+            }
+            ++iter;
+            tile_id += num_workers;
+        }
     }
 };
 

@@ -112,6 +112,8 @@ struct tsgemm_plan {
     int64_t m_blocks, n_blocks, k_blocks, tiles;
     int P;         // 0 = default (compute units)
     int xcd_remap; // 1 = permute workgroups so each XCD runs consecutive worker ids
+    int cluster;   // workgroups per cluster (tile scheduler option), >= 1
+    int col_major; // 1 = transposed tile walk (tile scheduler option)
     const KernelEntry* kernel;
 };
 
@@ -121,6 +123,14 @@ struct Grid {
     uint32_t P, xcds, max_iters;
 };
 
+// Waves of the longest-running workgroup: its cluster's share of the
+// ceil(m_blocks / cluster) x n_blocks cluster tiles.
+uint32_t max_iters_for(const tsgemm_plan* p, uint32_t P) {
+    const int64_t clusters = P / (uint32_t)p->cluster;
+    const int64_t m_cl = (p->m_blocks + p->cluster - 1) / p->cluster;
+    return (uint32_t)((m_cl * p->n_blocks + clusters - 1) / clusters);
+}
+
 int resolve_grid(const tsgemm_plan* p, Grid* g) {
     int cus = 0, xcds = 1;
     if (p->P == 0 || p->xcd_remap) {
@@ -129,7 +139,9 @@ int resolve_grid(const tsgemm_plan* p, Grid* g) {
     }
     g->P = (uint32_t)(p->P ? p->P : cus);
     g->xcds = p->xcd_remap ? (uint32_t)xcds : 1u;
-    g->max_iters = (uint32_t)((p->tiles + g->P - 1) / g->P);
+    if (g->P % (uint32_t)p->cluster != 0)
+        return fail(TSGEMM_EINVAL, "the %u workgroups do not split into clusters of %d", g->P, p->cluster);
+    g->max_iters = max_iters_for(p, g->P);
     return TSGEMM_OK;
 }
 
@@ -159,6 +171,8 @@ int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* 
     a.P = g.P;
     a.max_iters = g.max_iters;
     a.num_xcd = g.xcds;
+    a.cluster = (uint32_t)p->cluster;
+    a.col_major = (uint32_t)p->col_major;
     (void)hipGetLastError();
     if (p->k_blocks == 0) {
         // empty sum: C = 0 (N % 8 == 0, so 8 elements per thread)
@@ -222,7 +236,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     p->dtype = dtype; p->bm = block_M; p->bn = block_N; p->bk = block_K;
     p->group = group_size; p->stages = num_stages; p->slots = slots;
     p->m_blocks = mb; p->n_blocks = nb; p->k_blocks = K / block_K; p->tiles = mb * nb;
-    p->P = 0; p->xcd_remap = 1; p->kernel = k;
+    p->P = 0; p->xcd_remap = 1; p->cluster = 1; p->col_major = 0; p->kernel = k;
     return p;
 }
 
@@ -250,6 +264,16 @@ int tsgemm_set_xcd_remap(tsgemm_plan* p, int enable) {
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (enable != 0 && enable != 1) return fail(TSGEMM_EINVAL, "enable must be 0 or 1");
     p->xcd_remap = enable;
+    return TSGEMM_OK;
+}
+
+int tsgemm_set_schedule(tsgemm_plan* p, int column_major, int cluster_size) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (column_major != 0 && column_major != 1) return fail(TSGEMM_EINVAL, "column_major must be 0 or 1");
+    if (cluster_size < 1 || cluster_size > 64) return fail(TSGEMM_EINVAL, "cluster_size must be in [1, 64], got %d", cluster_size);
+    p->col_major = column_major;
+    p->cluster = cluster_size;
     return TSGEMM_OK;
 }
 
@@ -293,9 +317,11 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
     info->m_blocks = p->m_blocks; info->n_blocks = p->n_blocks;
     info->k_blocks = p->k_blocks; info->num_tiles = p->tiles;
     info->num_workgroups = p->P;  // explicit P only; default resolves at run time
-    info->waves = p->P ? (int32_t)((p->tiles + p->P - 1) / p->P) : 0;
+    info->waves = p->P && p->P % p->cluster == 0 ? (int32_t)max_iters_for(p, (uint32_t)p->P) : 0;
     info->threads_per_workgroup = 64 * p->kernel->waves;
     info->xcd_remap = p->xcd_remap;
+    info->cluster_size = p->cluster;
+    info->column_major = p->col_major;
     return TSGEMM_OK;
 }
 
@@ -303,8 +329,11 @@ int tsgemm_schedule_host(const tsgemm_plan* p, int num_workgroups, int32_t* out)
     g_err[0] = '\0';
     if (!p || !out) return fail(TSGEMM_EINVAL, "plan or out is NULL");
     if (num_workgroups <= 0) return fail(TSGEMM_EINVAL, "num_workgroups must be > 0");
+    if (num_workgroups % p->cluster != 0)
+        return fail(TSGEMM_EINVAL, "the %d workgroups do not split into clusters of %d", num_workgroups, p->cluster);
     tsg::TileScheduler s;
-    s.setup((uint32_t)num_workgroups, (uint32_t)p->m_blocks, (uint32_t)p->n_blocks, (uint32_t)p->group);
+    s.setup((uint32_t)num_workgroups, (uint32_t)p->m_blocks, (uint32_t)p->n_blocks, (uint32_t)p->group,
+            (uint32_t)p->cluster, (uint32_t)p->col_major);
     int64_t row = 0;
     for (uint32_t wid = 0; wid < (uint32_t)num_workgroups; ++wid)
         for (s.init(wid); s.valid(); s.next_tile(), ++row) {
@@ -332,7 +361,8 @@ int tsgemm_dump_schedule(const tsgemm_plan* p, int32_t* out) {
     e = hipMemset(d, 0xFF, n * sizeof(int32_t));
     if (e == hipSuccess) {
         hipLaunchKernelGGL(tsg::tsgemm_schedule_kernel, dim3(g.P), dim3(64), 0, 0, g.P, (uint32_t)p->m_blocks,
-                           (uint32_t)p->n_blocks, (uint32_t)p->group, g.xcds, g.max_iters, d);
+                           (uint32_t)p->n_blocks, (uint32_t)p->group, (uint32_t)p->cluster,
+                           (uint32_t)p->col_major, g.xcds, g.max_iters, d);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipMemcpy(h.data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost);

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
 
     // ---- loader: its own scheduler copy, L slabs ahead of the MMA ----
     TileScheduler ld;
-    ld.setup(args.P, args.m_blocks, args.n_blocks, args.group);
+    ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     ld.init(wid);
     uint32_t ld_k = 0, ld_phase = 0;
     i32x4 rs_a, rs_b;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // outside C get a vector offset past the descriptor's range and are
     // dropped; the row block goes into the scalar offset.
     TileScheduler sched;
-    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group);
+    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     const bool swap = (lg & 1u) != 0;  // odd lane groups hold the upper four columns of block 2t
     const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
     const uint32_t lane_off = (row0 * N + col0) * 2u;
@@ -369,12 +369,12 @@ __global__ void tsgemm_zero_kernel(uint16_t* C, int64_t count8) {
 
 // Schedule dump: the same scheduler and worker numbering as the GEMM kernel.
 __global__ void tsgemm_schedule_kernel(uint32_t P, uint32_t m_blocks, uint32_t n_blocks,
-                                       uint32_t group, uint32_t num_xcd, uint32_t max_iters,
-                                       int32_t* out) {
+                                       uint32_t group, uint32_t cluster, uint32_t col_major,
+                                       uint32_t num_xcd, uint32_t max_iters, int32_t* out) {
     if (threadIdx.x != 0) return;
     const uint32_t wid = worker_of_workgroup(blockIdx.x, P, num_xcd);
     TileScheduler s;
-    s.setup(P, m_blocks, n_blocks, group);
+    s.setup(P, m_blocks, n_blocks, group, cluster, col_major);
     for (s.init(wid); s.valid(); s.next_tile()) {
         int32_t* row = out + 4 * ((size_t)wid * max_iters + s.iter);
         *(int4*)row = make_int4((int)wid, (int)s.iter, (int)s.m_idx, (int)s.n_idx);

@@ -3,6 +3,7 @@ function include/tsgemm.h declares; create() validates its arguments; plan
 arithmetic; and the scheduler code compiled for the host reproduces the
 oracle schedule bit for bit."""
 
+import ctypes
 import os
 import re
 
@@ -131,3 +132,32 @@ def test_host_schedule_sweep_partial_groups():
         plan = tsg.Plan(mb * 128, nb * 128, 64, "bf16", 128, 128, 64, gs, 2)
         want = np.array(oracle.schedule.schedule(P, mb, nb, gs), dtype=np.int32)
         assert np.array_equal(plan.schedule_host(P), want), (mb, nb, gs, P)
+
+
+# ---------------------------------------------------------------- scheduler options
+def test_set_schedule_validation_and_info():
+    lib = tsg.load()
+    plan = tsg.Plan(1000, 1024, 256, "fp16", 128, 128, 64, 4, 2, num_workgroups=12)
+    inf = plan.info()
+    assert (inf["cluster_size"], inf["column_major"]) == (1, 0)
+    assert lib.tsgemm_set_schedule(plan._h, 2, 1) == tsg.EINVAL
+    assert lib.tsgemm_set_schedule(plan._h, 0, 0) == tsg.EINVAL and "cluster_size" in tsg.last_error()
+    assert lib.tsgemm_set_schedule(plan._h, 1, 3) == 0
+    inf = plan.info()
+    assert (inf["cluster_size"], inf["column_major"]) == (3, 1)
+    # 8 x 8 blocks, clusters of 3 -> 3 cluster rows x 8 = 24 cluster tiles over 4 clusters
+    assert inf["waves"] == 6
+    out = (ctypes.c_int32 * (4 * plan.num_tiles))()
+    assert lib.tsgemm_schedule_host(plan._h, 10, out) == tsg.EINVAL and "clusters of 3" in tsg.last_error()
+
+
+@pytest.mark.parametrize("cs", [1, 2, 3, 4])
+@pytest.mark.parametrize("cm", [False, True])
+def test_host_schedule_options_match_oracle(cs, cm):
+    rng = np.random.default_rng(100 + 10 * cs + cm)
+    for _ in range(40):
+        mb, nb = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        gs, P = int(rng.integers(1, 14)), cs * int(rng.integers(1, 12))
+        plan = tsg.Plan(mb * 128, nb * 128, 64, "bf16", 128, 128, 64, gs, 2, column_major=cm, cluster_size=cs)
+        want = np.array(oracle.schedule.schedule(P, mb, nb, gs, column_major=cm, cluster_size=cs), dtype=np.int32)
+        assert np.array_equal(plan.schedule_host(P), want), (mb, nb, gs, P, cs, cm)

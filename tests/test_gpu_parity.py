@@ -166,6 +166,12 @@ def test_output_rounding_is_nearest_even(dtype):
 
 
 # ---------------------------------------------------------------- schedule
+def _waves(plan, P):
+    inf = plan.info()
+    cs = inf["cluster_size"]
+    return -(-(-(-inf["m_blocks"] // cs) * inf["n_blocks"]) // (P // cs))
+
+
 def _plan_for(w, waves=0):
     return tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
                     w.num_stages, num_workgroups=w.num_workgroups, waves=waves)
@@ -190,8 +196,7 @@ def test_gemm_kernel_trace_matches_oracle(cfg, waves):
     print(f"[case] trace {cfg} waves={waves}", flush=True)
     plan = _plan_for(w, waves)
     P = plan.num_workgroups
-    T = plan.num_tiles
-    iters = -(-T // P)
+    iters = _waves(plan, P)
     A, B = workload_inputs(w)
     trace = torch.full((P * iters * 4,), -1, dtype=torch.int32, device=DEV)
     C = torch.empty((w.M, w.N), dtype=TDT[w.dtype], device=DEV)
@@ -257,3 +262,43 @@ def test_deterministic_repeat():
     C1, _ = _run(plan, A, B, w.dtype)
     C2, _ = _run(plan, A, B, w.dtype)
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- scheduler options
+OPTION_CASES = [(False, 2), (True, 1), (True, 2), (False, 3)]
+
+
+@pytest.mark.parametrize("cm,cs", OPTION_CASES)
+def test_schedule_options_dump_and_trace_bit_exact(cm, cs):
+    """Device dump and the GEMM kernel's own trace follow the oracle's cluster /
+    column-major schedule, including a tail cluster (m_blocks = 7)."""
+    M, N, K = 7 * 128 - 40, 6 * 128, 256
+    print(f"[case] options cm={cm} cs={cs}", flush=True)
+    P = 6 * cs
+    plan = tsg.Plan(M, N, K, "fp16", 128, 128, 64, 4, 2, num_workgroups=P, column_major=cm, cluster_size=cs)
+    want = np.array(oracle.schedule.schedule(P, 7, 6, 4, column_major=cm, cluster_size=cs), dtype=np.int32)
+    assert np.array_equal(plan.dump_schedule(), want)
+    A, B = make_inputs(M, N, K, "fp16", "uniform", 400 + cs)
+    iters = _waves(plan, P)
+    trace = torch.full((P * iters * 4,), -1, dtype=torch.int32, device=DEV)
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    plan.run_traced(A.to(DEV), B.to(DEV), C, trace)
+    torch.cuda.synchronize()
+    rows = trace.view(-1, 4).cpu().numpy()
+    assert np.array_equal(rows[rows[:, 0] >= 0], want)
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), oracle.FP16)
+    _check_close(C.cpu().double().numpy(), _bits_to_f64(ref_bits, "fp16"), "options")
+
+
+@pytest.mark.parametrize("cm,cs", OPTION_CASES)
+@pytest.mark.parametrize("waves", [4, 8])
+def test_schedule_options_parity_256(cm, cs, waves):
+    print(f"[case] options 256 cm={cm} cs={cs} waves={waves}", flush=True)
+    M, N, K = 5 * 256 - 72, 3 * 256 + 16, 448
+    A, B = make_inputs(M, N, K, "bf16", "normal_sqrtk", 500 + cs)
+    plan = tsg.Plan(M, N, K, "bf16", 256, 256, 64, 2, 3, num_workgroups=4 * cs, waves=waves,
+                    column_major=cm, cluster_size=cs)
+    C, guard = _run(plan, A, B, "bf16", guard=64)
+    assert torch.isnan(guard.float()).all()
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), oracle.BF16)
+    _check_close(C.double().numpy(), _bits_to_f64(ref_bits, "bf16"), "options 256")
