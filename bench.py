@@ -8,8 +8,13 @@ Prints one JSON line:
   roofline   the GEMM kernel against the dense bf16 MFMA peak: achieved =
              2*M*N*K per launch / mean launch time from HIP events recorded on
              the launch stream around every timed launch
+  context    torch's own A @ B (hipBLASLt) on the same device inputs, for
+             reference only
   cpu_baseline  the CPU oracle (fp64 triple loop) timed on this host on a
              bounded sample of the same product (its first R rows of C)
+--workload picks another of the six shapes; --cold rewrites a 512 MiB buffer
+before every timed launch so the small shapes are not served from the
+Infinity Cache.
 """
 
 from __future__ import annotations
@@ -81,6 +86,22 @@ def cpu_baseline(w, A, B, target_s: float = 15.0):
     }
 
 
+def torch_context(torch, Ad, Bd, w, stream, warmup, steps):
+    """torch's own A @ B (hipBLASLt) on the same device inputs, as context only."""
+    for _ in range(min(warmup, 10)):
+        torch.matmul(Ad, Bd)
+    torch.cuda.synchronize()
+    n = max(5, min(steps, 20))
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(n):
+        torch.matmul(Ad, Bd)
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / n
+    return {"torch_matmul_ms": round(ms, 4), "torch_matmul_tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def copy_mode(args, torch):
     """Plain device-to-device copy of a known size: reads and writes
     copy-mib MiB per launch.  Its FETCH_SIZE / WRITE_SIZE counter readings give
@@ -114,6 +135,10 @@ def main():
     ap.add_argument("--mode", choices=["gemm", "copy"], default="gemm",
                     help="copy: time a plain device copy of --copy-mib MiB (calibrates HBM byte counters)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--cold", action="store_true",
+                    help="rewrite a 512 MiB scratch buffer before every timed launch (caches cold); "
+                         "the per-launch events still bracket only the GEMM")
+    ap.add_argument("--no-torch-context", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -144,9 +169,12 @@ def main():
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
         starts[i].record(stream)
         plan.run(Ad, Bd, C, stream)
         ends[i].record(stream)
@@ -154,6 +182,9 @@ def main():
     wall = time.perf_counter() - t0
     launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     mean_ms = sum(launch_ms) / len(launch_ms)
+    if scratch is not None:
+        # wall time includes the cache flushes: report the GEMM launches only
+        wall = sum(launch_ms) * 1e-3
 
     flops = float(w.flops)
     value = flops * args.steps / wall / 1e12
@@ -187,11 +218,16 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": recorded_traffic(w.name),
             "kernel_ms": {"mean": round(mean_ms, 4), "min": round(launch_ms[0], 4),
-                          "median": round(launch_ms[len(launch_ms) // 2], 4)},
+                          "median": round(launch_ms[len(launch_ms) // 2], 4),
+                          "p90": round(launch_ms[min(len(launch_ms) - 1, (9 * len(launch_ms)) // 10)], 4)},
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9, 1),
+            "caches": "cold (512 MiB rewritten before each launch)" if args.cold else "warm",
         },
+        "context": None,
         "cpu_baseline": None,
     }
+    if not args.no_torch_context:
+        out["context"] = torch_context(torch, Ad, Bd, w, stream, args.warmup, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B)
     print(json.dumps(out), flush=True)
