@@ -12,9 +12,12 @@ Prints one JSON line:
              reference only
   cpu_baseline  the CPU oracle (fp64 triple loop) timed on this host on a
              bounded sample of the same product (its first R rows of C)
---workload picks another of the six shapes; --cold rewrites a 512 MiB buffer
-before every timed launch so the small shapes are not served from the
-Infinity Cache.
+--workload picks another of the six shapes, or the block-scaled FP8 shape
+mx_8192_mxfp8 (tsgemm_run_mx: E4M3 elements with E8M0 scales per 32 along K,
+bf16 output; roofline against the dense fp8 MFMA peak; cpu_baseline the MX
+oracle; context torch's per-tensor-scaled fp8 product when available).  --cold
+rewrites a 512 MiB buffer before every timed launch so the small shapes are not
+served from the Infinity Cache.
 """
 
 from __future__ import annotations
@@ -29,17 +32,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "mxfp8": 5000.0}   # MI355X dense MFMA, published
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "cfg3_8192_bf16"
-KERNEL_SOURCES = ("persistent_tile_scheduled_amd/csrc/tsgemm_kernel.h",
-                  "persistent_tile_scheduled_amd/csrc/tsgemm_device.h",
-                  "persistent_tile_scheduled_amd/csrc/tile_scheduler.h",
-                  "persistent_tile_scheduled_amd/csrc/tsgemm.hip")
-PROFILE_FOR = {"cfg3_8192_bf16": "profiles/gemm_8192_bf16.md"}
+_CSRC = "persistent_tile_scheduled_amd/csrc/"
+KERNEL_SOURCES = {
+    "gemm": tuple(_CSRC + f for f in ("tsgemm_kernel.h", "tsgemm_device.h", "tile_scheduler.h", "tsgemm.hip")),
+    "mx": tuple(_CSRC + f for f in ("tsgemm_mx_kernel.h", "tsgemm_device.h", "tile_scheduler.h", "tsgemm.hip")),
+}
+PROFILE_FOR = {"cfg3_8192_bf16": "profiles/gemm_8192_bf16.md", "mx_8192_mxfp8": "profiles/gemm_8192_mxfp8.md"}
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, kind: str = "gemm"):
     """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE + WRITE_SIZE,
     calibrated on a plain copy) as recorded in profiles/, or None when there is
     no record or the kernel sources changed since it was taken."""
@@ -48,7 +52,7 @@ def recorded_traffic(workload: str):
     if not path or not os.path.exists(os.path.join(ROOT, path)):
         return None
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     fields = {}
@@ -84,6 +88,56 @@ def cpu_baseline(w, A, B, target_s: float = 15.0):
         "kind": "oracle",
         "sample": f"first {rows} of {w.M} rows of C ({flops / 1e9:.1f} GFLOP, fp64 triple loop, {dt:.1f} s)",
     }
+
+
+def cpu_baseline_mx(w, A, SFA, B, SFB, target_s: float = 15.0):
+    """Time the MX oracle on the first R rows of C, R sized for ~target_s seconds."""
+    import numpy as np
+    import oracle
+    rows = min(w.M, 64)
+    t0 = time.perf_counter()
+    oracle.mx_gemm_f64(A[:rows], SFA[:rows], B, SFB)
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    c = oracle.mx_gemm_f64(A[:rows], SFA[:rows], B, SFB)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(c).all()
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.M} rows of C ({flops / 1e9:.1f} GFLOP, MX decode + fp64 sum, {dt:.1f} s)",
+    }
+
+
+def torch_context_fp8(torch, Ad, Bd, w, stream, warmup, steps):
+    """torch._scaled_mm on the same E4M3 codes with one fp32 scale per tensor
+    (hipBLASLt fp8; not the block-scaled product), as context only."""
+    try:
+        a = Ad.view(torch.float8_e4m3fn)
+        b = Bd.view(torch.float8_e4m3fn).t()
+        one = torch.ones((), dtype=torch.float32, device=Ad.device)
+
+        def f():
+            return torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        for _ in range(min(warmup, 10)):
+            f()
+        torch.cuda.synchronize()
+        n = max(5, min(steps, 20))
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(n):
+            f()
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / n
+        return {"torch_scaled_mm_fp8_per_tensor_ms": round(ms, 4),
+                "torch_scaled_mm_fp8_per_tensor_tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+    except Exception as exc:  # context only: an unsupported op is reported, not fatal
+        return {"torch_scaled_mm_fp8_per_tensor": f"unavailable: {type(exc).__name__}: {str(exc)[:120]}"}
 
 
 def torch_context(torch, Ad, Bd, w, stream, warmup, steps):
@@ -150,21 +204,37 @@ def main():
         copy_mode(args, torch)
         return
     import persistent_tile_scheduled_amd as tsg
-    from workloads import WORKLOADS, workload_inputs
+    from workloads import MX_WORKLOADS, WORKLOADS, mx_workload_inputs, workload_inputs
 
-    w = WORKLOADS[args.workload]
+    mx = args.workload in MX_WORKLOADS
+    if not mx and args.workload not in WORKLOADS:
+        sys.exit(f"unknown workload {args.workload!r}; have {sorted(WORKLOADS) + sorted(MX_WORKLOADS)}")
     dev = torch.device("cuda:0")
-    A, B = workload_inputs(w)
-    Ad, Bd = A.to(dev), B.to(dev)
-    C = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=dev)
+    if mx:
+        w = MX_WORKLOADS[args.workload]
+        A, SFA, B, SFB = mx_workload_inputs(w)
+        operands = [torch.from_numpy(x).to(dev) for x in (A, SFA, B, SFB)]
+        Ad, Bd = operands[0], operands[2]
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    else:
+        w = WORKLOADS[args.workload]
+        A, B = workload_inputs(w)
+        Ad, Bd = A.to(dev), B.to(dev)
+        C = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=dev)
     plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
                     w.num_stages, num_workgroups=w.num_workgroups)
     info = plan.info()
     P = plan.num_workgroups
     stream = torch.cuda.current_stream(dev)
 
+    def launch():
+        if mx:
+            plan.run_mx(*operands, C, stream)
+        else:
+            plan.run(Ad, Bd, C, stream)
+
     for _ in range(args.warmup):
-        plan.run(Ad, Bd, C, stream)
+        launch()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -176,7 +246,7 @@ def main():
         if scratch is not None:
             scratch.fill_(i & 0xFF)
         starts[i].record(stream)
-        plan.run(Ad, Bd, C, stream)
+        launch()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -191,7 +261,8 @@ def main():
     achieved = flops / (mean_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     out = {
-        "metric": "GEMM TFLOP/s and % of dense fp16/bf16 MFMA peak, 1xMI355X",
+        "metric": ("MXFP8 block-scaled GEMM TFLOP/s and % of dense fp8 MFMA peak, 1xMI355X" if mx
+                   else "GEMM TFLOP/s and % of dense fp16/bf16 MFMA peak, 1xMI355X"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -208,7 +279,8 @@ def main():
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
             "tile": [w.block_M, w.block_N, w.block_K], "group_size": w.group_size,
             "num_stages": w.num_stages, "lds_slots": info["lds_slots"], "num_workgroups": P,
-            "inputs": f"{w.dist}, seed {w.seed}",
+            "inputs": (f"normal(0,1) MX-encoded (E4M3 + E8M0 per 32 along K), seed {w.seed}" if mx
+                       else f"{w.dist}, seed {w.seed}"),
         },
         "roofline": {
             "bound": "mfma",
@@ -216,7 +288,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": recorded_traffic(w.name),
+            "traffic": recorded_traffic(w.name, "mx" if mx else "gemm"),
             "kernel_ms": {"mean": round(mean_ms, 4), "min": round(launch_ms[0], 4),
                           "median": round(launch_ms[len(launch_ms) // 2], 4),
                           "p90": round(launch_ms[min(len(launch_ms) - 1, (9 * len(launch_ms)) // 10)], 4)},
@@ -227,9 +299,10 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_torch_context:
-        out["context"] = torch_context(torch, Ad, Bd, w, stream, args.warmup, args.steps)
+        out["context"] = (torch_context_fp8 if mx else torch_context)(torch, Ad, Bd, w, stream,
+                                                                      args.warmup, args.steps)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B)
+        out["cpu_baseline"] = cpu_baseline_mx(w, A, SFA, B, SFB) if mx else cpu_baseline(w, A, B)
     print(json.dumps(out), flush=True)
 
 

@@ -42,7 +42,8 @@ extern "C" {
 
 typedef struct tsgemm_plan tsgemm_plan; /* opaque, owned by the library */
 
-enum { TSGEMM_FP16 = 1, TSGEMM_BF16 = 2 };
+/* TSGEMM_MXFP8: block-scaled FP8 inputs with bf16 output (tsgemm_run_mx). */
+enum { TSGEMM_FP16 = 1, TSGEMM_BF16 = 2, TSGEMM_MXFP8 = 3 };
 
 enum {
     TSGEMM_OK = 0,
@@ -60,7 +61,8 @@ typedef struct tsgemm_info {
     int32_t group_size;
     int32_t num_stages;      /* as requested                                         */
     int32_t lds_slots;       /* K-slabs resident in LDS: min(num_stages, LDS / stage) */
-    int32_t stage_bytes;     /* (block_M*block_K + block_K*block_N) * 2              */
+    int32_t stage_bytes;     /* (block_M*block_K + block_K*block_N) * 2; MXFP8:
+                                (block_M + block_N) * (block_K + 4)               */
     int32_t lds_bytes;       /* lds_slots * stage_bytes                              */
     int64_t m_blocks, n_blocks, k_blocks, num_tiles;
     int32_t num_workgroups;  /* P; 0 while unresolved (default P before a device is seen) */
@@ -79,8 +81,10 @@ typedef struct tsgemm_info {
  *                as the lowered host function's "divisible by 8" check);
  *                block_M*K*2, block_K*N*2 and block_M*N*2 below 2^31 (per-tile
  *                32-bit offsets); M, N < 2^31.
- *   dtype        TSGEMM_FP16 or TSGEMM_BF16 (A, B and C).
- *   block_M/N/K  one of 128x128x32, 128x128x64, 256x256x32, 256x256x64.
+ *   dtype        TSGEMM_FP16 or TSGEMM_BF16 (A, B and C), or TSGEMM_MXFP8
+ *                (see tsgemm_run_mx; 1-byte elements enter the 2^31 bounds).
+ *   block_M/N/K  one of 128x128x32, 128x128x64, 256x256x32, 256x256x64;
+ *                MXFP8: 256x256x128 only (K % 128 == 0, two LDS stages).
  *   group_size   >= 1, column blocks per rasterisation group.
  *   num_stages   >= 2: K-slabs in flight; the LDS ring holds
  *                min(num_stages, floor(160 KiB / stage_bytes)) of them.
@@ -127,6 +131,38 @@ int tsgemm_run(const tsgemm_plan* plan, const void* A, const void* B, void* C, v
  * row worker*max_iters + iter.  Diagnostic; rows not visited are left untouched. */
 int tsgemm_run_traced(const tsgemm_plan* plan, const void* A, const void* B, void* C,
                       void* stream, int32_t* trace);
+
+/* Block-scaled FP8 (MX) product of a TSGEMM_MXFP8 plan, on `stream`:
+ *
+ *   C[m][n] = sum_k x(A[m][k]) * s(SFA[m][k/32]) * x(B[n][k]) * s(SFB[n][k/32])
+ *
+ * rounded once to bf16 (nearest, ties to even), fp32 accumulation.  The page
+ * "[Feature] Introduce tile scheduler #2441" lists this MXFP8 block-scaled
+ * persistent GEMM ("1d1d" scale factors SFA, SFB) among the examples driven
+ * by the same tile scheduler, without its formats; they follow the OCP
+ * Microscaling Formats specification v1.0:
+ *   x(): FP8 E4M3 element (bias 7, subnormals, S.1111.111 = NaN, max 448);
+ *   s(): E8M0 scale 2^(e - 127), 0xFF = NaN; one scale per 32 consecutive
+ *        elements along K ("1d" blocks on both operands).
+ * Layout (row-major, contiguous, DEVICE pointers, caller-owned):
+ *   A   uint8[M][K]     B   uint8[N][K]   (both K-contiguous: B is given
+ *   SFA uint8[M][K/32]  SFB uint8[N][K/32] transposed relative to tsgemm_run)
+ *   C   bf16[M][N]
+ * A, B, C 16-byte aligned, SFA and SFB 4-byte aligned.  Inner products are
+ * formed by the gfx950 matrix core, which adds the up to 64 scaled products of
+ * one instruction with an internal error (measured: at most about 2^-12 of
+ * the sum of their magnitudes) before the fp32 accumulation, so C matches the
+ * exact product to within that plus the final bf16 rounding, not bit for bit.  Scheduler
+ * options, the number of workgroups and the XCD remap apply as for tsgemm_run;
+ * tsgemm_set_waves accepts only 4.  M*N == 0 launches nothing; K == 0 gives
+ * C = 0.  Returns TSGEMM_EINVAL for a plan of another dtype (and tsgemm_run
+ * for an MXFP8 plan). */
+int tsgemm_run_mx(const tsgemm_plan* plan, const void* A, const void* SFA, const void* B,
+                  const void* SFB, void* C, void* stream);
+
+/* tsgemm_run_mx plus the per-tile trace of tsgemm_run_traced. */
+int tsgemm_run_mx_traced(const tsgemm_plan* plan, const void* A, const void* SFA, const void* B,
+                         const void* SFB, void* C, void* stream, int32_t* trace);
 
 int64_t tsgemm_num_tiles(const tsgemm_plan* plan);       /* < 0 on error                */
 int tsgemm_num_workgroups(const tsgemm_plan* plan);      /* resolves the default P      */

@@ -6,8 +6,8 @@ validation are host-only); running needs the built library and a gfx950 GPU,
 and fails loudly otherwise.
 
 Names follow the C ABI: ``create`` -> :class:`Plan`, ``Plan.run``,
-``Plan.run_traced``, ``Plan.dump_schedule``, ``Plan.schedule_host``,
-``Plan.info``, ``last_error``.
+``Plan.run_traced``, ``Plan.run_mx``, ``Plan.run_mx_traced``,
+``Plan.dump_schedule``, ``Plan.schedule_host``, ``Plan.info``, ``last_error``.
 """
 
 from __future__ import annotations
@@ -24,13 +24,14 @@ LIB_PATH = os.path.join(_HERE, "libtsgemm.so")
 
 FP16 = 1
 BF16 = 2
+MXFP8 = 3   # E4M3 elements + E8M0 scales per 32 along K, bf16 output
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, -1, -2, -3, -4
 
 # every symbol the header declares
 EXPORTS = (
     "tsgemm_create", "tsgemm_set_num_workgroups", "tsgemm_set_waves", "tsgemm_set_schedule",
     "tsgemm_set_xcd_remap", "tsgemm_run",
-    "tsgemm_run_traced", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
+    "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
 )
 
@@ -88,6 +89,10 @@ def load(path: str | None = None):
     lib.tsgemm_run.restype = i32
     lib.tsgemm_run_traced.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.tsgemm_run_traced.restype = i32
+    lib.tsgemm_run_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.tsgemm_run_mx.restype = i32
+    lib.tsgemm_run_mx_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.tsgemm_run_mx_traced.restype = i32
     lib.tsgemm_num_tiles.argtypes = [vp]
     lib.tsgemm_num_tiles.restype = i64
     lib.tsgemm_num_workgroups.argtypes = [vp]
@@ -117,7 +122,7 @@ def _check(rc: int) -> int:
     return rc
 
 
-_DTYPES = {"fp16": FP16, "bf16": BF16, FP16: FP16, BF16: BF16}
+_DTYPES = {"fp16": FP16, "bf16": BF16, "mxfp8": MXFP8, FP16: FP16, BF16: BF16, MXFP8: MXFP8}
 
 
 class Plan:
@@ -179,9 +184,30 @@ class Plan:
         _check(self._lib.tsgemm_dump_schedule(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return out
 
+    def trace_rows(self) -> int:
+        """Rows (of 4 int32) a traced run may write: P * max_iters for the
+        plan's resolved number of workgroups P and cluster size cs."""
+        inf = self.info()
+        P, cs = self.num_workgroups, inf["cluster_size"]
+        if P % cs:
+            raise TsgemmError(EINVAL, f"the {P} workgroups do not split into clusters of {cs}")
+        m_cl = -(-inf["m_blocks"] // cs)
+        return P * (-(-(m_cl * inf["n_blocks"]) // (P // cs)))
+
+    def _check_trace(self, trace):
+        import torch
+        if trace.dtype != torch.int32 or not trace.is_cuda or not trace.is_contiguous():
+            raise ValueError("trace must be a contiguous int32 CUDA tensor")
+        need = 4 * self.trace_rows()
+        if trace.numel() < need:
+            raise ValueError(f"trace holds {trace.numel()} int32, the run may write {need}")
+        return trace.data_ptr()
+
     # -- run -----------------------------------------------------------------
     def _args(self, A, B, C):
         import torch
+        if self.dtype == MXFP8:
+            raise ValueError("an MXFP8 plan runs with run_mx")
         want = torch.float16 if self.dtype == FP16 else torch.bfloat16
         for name, t, shape in (("A", A, (self.M, self.K)), ("B", B, (self.K, self.N)), ("C", C, (self.M, self.N))):
             if t.dtype != want or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
@@ -198,10 +224,40 @@ class Plan:
     def run_traced(self, A, B, C, trace, stream=None) -> None:
         import torch
         a, b, c = self._args(A, B, C)
-        if trace.dtype != torch.int32 or not trace.is_cuda or not trace.is_contiguous():
-            raise ValueError("trace must be a contiguous int32 CUDA tensor")
+        t = self._check_trace(trace)
         s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
-        _check(self._lib.tsgemm_run_traced(self._h, a, b, c, s, trace.data_ptr()))
+        _check(self._lib.tsgemm_run_traced(self._h, a, b, c, s, t))
+
+    def _mx_args(self, A, SFA, B, SFB, C):
+        import torch
+        if self.dtype != MXFP8:
+            raise ValueError("run_mx needs a plan created with dtype 'mxfp8'")
+        M, N, K = self.M, self.N, self.K
+        out = []
+        for name, t, shape in (("A", A, (M, K)), ("SFA", SFA, (M, K // 32)),
+                               ("B", B, (N, K)), ("SFB", SFB, (N, K // 32))):
+            if t.element_size() != 1 or t.dtype == torch.bool or tuple(t.shape) != shape \
+                    or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous 1-byte CUDA tensor of shape {shape}")
+            out.append(t.data_ptr())
+        if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, N) or not C.is_contiguous() or not C.is_cuda:
+            raise ValueError(f"C must be a contiguous torch.bfloat16 CUDA tensor of shape {(M, N)}")
+        return out + [C.data_ptr()]
+
+    def run_mx(self, A, SFA, B, SFB, C, stream=None) -> None:
+        """Block-scaled FP8 product (tsgemm_run_mx): A[M,K], B[N,K] E4M3 codes,
+        SFA[M,K/32], SFB[N,K/32] E8M0 codes (any 1-byte dtype), C[M,N] bf16."""
+        import torch
+        a, sa, b, sb, c = self._mx_args(A, SFA, B, SFB, C)
+        s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        _check(self._lib.tsgemm_run_mx(self._h, a, sa, b, sb, c, s))
+
+    def run_mx_traced(self, A, SFA, B, SFB, C, trace, stream=None) -> None:
+        import torch
+        a, sa, b, sb, c = self._mx_args(A, SFA, B, SFB, C)
+        t = self._check_trace(trace)
+        s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        _check(self._lib.tsgemm_run_mx_traced(self._h, a, sa, b, sb, c, s, t))
 
 
 def matmul(A, B, block_M=256, block_N=256, block_K=64, group_size=8, num_stages=3):

@@ -17,6 +17,7 @@
 #include "tsgemm.h"
 #include "tile_scheduler.h"
 #include "tsgemm_kernel.h"
+#include "tsgemm_mx_kernel.h"
 
 namespace {
 
@@ -114,7 +115,7 @@ struct tsgemm_plan {
     int xcd_remap; // 1 = permute workgroups so each XCD runs consecutive worker ids
     int cluster;   // workgroups per cluster (tile scheduler option), >= 1
     int col_major; // 1 = transposed tile walk (tile scheduler option)
-    const KernelEntry* kernel;
+    const KernelEntry* kernel;  // fp16/bf16 kernel; NULL for an MXFP8 plan
 };
 
 namespace {
@@ -122,6 +123,14 @@ namespace {
 struct Grid {
     uint32_t P, xcds, max_iters;
 };
+
+bool is_mx(const tsgemm_plan* p) { return p->dtype == TSGEMM_MXFP8; }
+
+// Bytes of one LDS stage: the A and B slabs (and for MXFP8 their scale bytes,
+// 4 per row and 128-deep slab).
+int stage_bytes_of(int dtype, int bm, int bn, int bk) {
+    return dtype == TSGEMM_MXFP8 ? (bm + bn) * (bk + 4) : (bm * bk + bk * bn) * 2;
+}
 
 // Waves of the longest-running workgroup: its cluster's share of the
 // ceil(m_blocks / cluster) x n_blocks cluster tiles.
@@ -148,6 +157,7 @@ int resolve_grid(const tsgemm_plan* p, Grid* g) {
 int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* stream, int32_t* trace) {
     g_err[0] = '\0';
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (is_mx(p)) return fail(TSGEMM_EINVAL, "an MXFP8 plan runs with tsgemm_run_mx");
     if (p->M == 0 || p->N == 0) return TSGEMM_OK;  // empty output: nothing to launch
     if (!C) return fail(TSGEMM_EINVAL, "C is NULL");
     if (p->K > 0 && (!A || !B)) return fail(TSGEMM_EINVAL, "A or B is NULL");
@@ -188,6 +198,55 @@ int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* 
     return TSGEMM_OK;
 }
 
+int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB, void* C,
+                void* stream, int32_t* trace) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (!is_mx(p)) return fail(TSGEMM_EINVAL, "tsgemm_run_mx needs a TSGEMM_MXFP8 plan (dtype %d)", p->dtype);
+    if (p->M == 0 || p->N == 0) return TSGEMM_OK;
+    if (!C) return fail(TSGEMM_EINVAL, "C is NULL");
+    if (p->K > 0 && (!A || !B || !SFA || !SFB)) return fail(TSGEMM_EINVAL, "A, SFA, B or SFB is NULL");
+    if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) | reinterpret_cast<uintptr_t>(C)) & 15u)
+        return fail(TSGEMM_EINVAL, "A, B and C must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)
+        return fail(TSGEMM_EINVAL, "SFA and SFB must be 4-byte aligned");
+    Grid g;
+    int rc = resolve_grid(p, &g);
+    if (rc != TSGEMM_OK) return rc;
+    (void)hipGetLastError();
+    if (p->k_blocks == 0) {
+        const int64_t count8 = p->M * p->N / 8;
+        const unsigned blocks = (unsigned)((count8 + 255) / 256);
+        hipLaunchKernelGGL(tsg::tsgemm_zero_kernel, dim3(blocks), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), static_cast<uint16_t*>(C), count8);
+    } else {
+        tsg::MxArgs a;
+        a.A = static_cast<const uint8_t*>(A);
+        a.SFA = static_cast<const uint8_t*>(SFA);
+        a.B = static_cast<const uint8_t*>(B);
+        a.SFB = static_cast<const uint8_t*>(SFB);
+        a.C = static_cast<uint16_t*>(C);
+        a.trace = trace;
+        a.M = p->M;
+        a.N = p->N;
+        a.K = p->K;
+        a.m_blocks = (uint32_t)p->m_blocks;
+        a.n_blocks = (uint32_t)p->n_blocks;
+        a.k_blocks = (uint32_t)p->k_blocks;
+        a.group = (uint32_t)p->group;
+        a.P = g.P;
+        a.max_iters = g.max_iters;
+        a.num_xcd = g.xcds;
+        a.cluster = (uint32_t)p->cluster;
+        a.col_major = (uint32_t)p->col_major;
+        hipLaunchKernelGGL(tsg::tsgemm_mx_kernel, dim3(g.P), dim3(tsg::MxTraits::THREADS), 0,
+                           static_cast<hipStream_t>(stream), a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TSGEMM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return TSGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,8 +260,9 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) {
         fail(TSGEMM_EINVAL, "M, N and K must be below 2^31"); return nullptr;
     }
-    if (dtype != TSGEMM_FP16 && dtype != TSGEMM_BF16) {
-        fail(TSGEMM_EINVAL, "dtype must be TSGEMM_FP16 (1) or TSGEMM_BF16 (2), got %d", dtype); return nullptr;
+    if (dtype != TSGEMM_FP16 && dtype != TSGEMM_BF16 && dtype != TSGEMM_MXFP8) {
+        fail(TSGEMM_EINVAL, "dtype must be TSGEMM_FP16 (1), TSGEMM_BF16 (2) or TSGEMM_MXFP8 (3), got %d", dtype);
+        return nullptr;
     }
     if (block_M <= 0 || block_N <= 0 || block_K <= 0) { fail(TSGEMM_EINVAL, "block sizes must be positive"); return nullptr; }
     if (group_size < 1) { fail(TSGEMM_EINVAL, "group_size must be >= 1, got %d", group_size); return nullptr; }
@@ -213,23 +273,35 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     if (N % 8 != 0 || K % 8 != 0) {
         fail(TSGEMM_EINVAL, "N and K must be divisible by 8 (16-byte rows)"); return nullptr;
     }
-    if (!tile_supported(block_M, block_N, block_K)) {
+    if (dtype == TSGEMM_MXFP8) {
+        if (block_M != 256 || block_N != 256 || block_K != 128) {
+            fail(TSGEMM_EUNSUPPORTED, "MXFP8 tile %dx%dx%d is not compiled (have 256x256x128)", block_M, block_N, block_K);
+            return nullptr;
+        }
+    } else if (!tile_supported(block_M, block_N, block_K)) {
         fail(TSGEMM_EUNSUPPORTED, "tile %dx%dx%d is not compiled (have 128x128x{32,64}, 256x256x{32,64})",
              block_M, block_N, block_K);
         return nullptr;
     }
     const int64_t lim = int64_t(1) << 31;
-    if (int64_t(block_M) * K * 2 >= lim || int64_t(block_K) * N * 2 >= lim || int64_t(block_M) * N * 2 >= lim) {
+    if (dtype == TSGEMM_MXFP8) {
+        if (int64_t(block_M) * K >= lim || int64_t(block_N) * K >= lim || int64_t(block_M) * N * 2 >= lim) {
+            fail(TSGEMM_EUNSUPPORTED, "a tile's byte extent (block_M*K, block_N*K, block_M*N*2) exceeds 2^31");
+            return nullptr;
+        }
+    } else if (int64_t(block_M) * K * 2 >= lim || int64_t(block_K) * N * 2 >= lim || int64_t(block_M) * N * 2 >= lim) {
         fail(TSGEMM_EUNSUPPORTED, "a tile's byte extent (block_M*K*2, block_K*N*2, block_M*N*2) exceeds 2^31");
         return nullptr;
     }
-    const int stage = (block_M * block_K + block_K * block_N) * 2;
-    const int slots = ring_slots(block_M, block_N, block_K, num_stages);
+    const int stage = stage_bytes_of(dtype, block_M, block_N, block_K);
+    const int slots = dtype == TSGEMM_MXFP8 ? 2 : ring_slots(block_M, block_N, block_K, num_stages);
     if (slots < 2) { fail(TSGEMM_EUNSUPPORTED, "two %d-byte stages do not fit in LDS", stage); return nullptr; }
     const int64_t mb = (M + block_M - 1) / block_M, nb = (N + block_N - 1) / block_N;
     if (mb * nb >= lim) { fail(TSGEMM_EUNSUPPORTED, "tile count must be below 2^31"); return nullptr; }
-    const KernelEntry* k = find_kernel(dtype, block_M, block_N, block_K, slots, default_waves(block_M, block_N, block_K));
-    if (!k) { fail(TSGEMM_EUNSUPPORTED, "no kernel for this configuration"); return nullptr; }
+    const KernelEntry* k = dtype == TSGEMM_MXFP8
+                               ? nullptr
+                               : find_kernel(dtype, block_M, block_N, block_K, slots, default_waves(block_M, block_N, block_K));
+    if (!k && dtype != TSGEMM_MXFP8) { fail(TSGEMM_EUNSUPPORTED, "no kernel for this configuration"); return nullptr; }
     tsgemm_plan* p = new (std::nothrow) tsgemm_plan;
     if (!p) { fail(TSGEMM_ENOMEM, "out of host memory"); return nullptr; }
     p->M = M; p->N = N; p->K = K;
@@ -253,6 +325,7 @@ int tsgemm_set_waves(tsgemm_plan* p, int waves) {
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (waves == 0) waves = default_waves(p->bm, p->bn, p->bk);
     if (waves != 4 && waves != 8) return fail(TSGEMM_EINVAL, "waves must be 0, 4 or 8, got %d", waves);
+    if (is_mx(p)) return waves == 4 ? TSGEMM_OK : fail(TSGEMM_EUNSUPPORTED, "the MXFP8 kernel runs 4 waves");
     const KernelEntry* k = find_kernel(p->dtype, p->bm, p->bn, p->bk, p->slots, waves);
     if (!k) return fail(TSGEMM_EUNSUPPORTED, "no %d-wave kernel for this configuration", waves);
     p->kernel = k;
@@ -287,6 +360,17 @@ int tsgemm_run_traced(const tsgemm_plan* p, const void* A, const void* B, void* 
     return run_impl(p, A, B, C, stream, trace);
 }
 
+int tsgemm_run_mx(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB, void* C,
+                  void* stream) {
+    return run_mx_impl(p, A, SFA, B, SFB, C, stream, nullptr);
+}
+
+int tsgemm_run_mx_traced(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB,
+                         void* C, void* stream, int32_t* trace) {
+    if (!trace) return fail(TSGEMM_EINVAL, "trace is NULL");
+    return run_mx_impl(p, A, SFA, B, SFB, C, stream, trace);
+}
+
 int64_t tsgemm_num_tiles(const tsgemm_plan* p) {
     g_err[0] = '\0';
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
@@ -312,13 +396,13 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
     info->group_size = p->group;
     info->num_stages = p->stages;
     info->lds_slots = p->slots;
-    info->stage_bytes = (p->bm * p->bk + p->bk * p->bn) * 2;
+    info->stage_bytes = stage_bytes_of(p->dtype, p->bm, p->bn, p->bk);
     info->lds_bytes = info->stage_bytes * p->slots;
     info->m_blocks = p->m_blocks; info->n_blocks = p->n_blocks;
     info->k_blocks = p->k_blocks; info->num_tiles = p->tiles;
     info->num_workgroups = p->P;  // explicit P only; default resolves at run time
     info->waves = p->P && p->P % p->cluster == 0 ? (int32_t)max_iters_for(p, (uint32_t)p->P) : 0;
-    info->threads_per_workgroup = 64 * p->kernel->waves;
+    info->threads_per_workgroup = p->kernel ? 64 * p->kernel->waves : tsg::MxTraits::THREADS;
     info->xcd_remap = p->xcd_remap;
     info->cluster_size = p->cluster;
     info->column_major = p->col_major;

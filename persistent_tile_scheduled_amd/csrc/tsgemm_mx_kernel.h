@@ -1,0 +1,369 @@
+// Persistent, tile-scheduled block-scaled FP8 (MX) GEMM for gfx950 (CDNA4).
+//
+//   C[m,n] = sum_k x(A[m,k]) * s(SFA[m,k/32]) * x(B[n,k]) * s(SFB[n,k/32])
+//
+// x() decodes an OCP FP8 E4M3 element, s() an OCP E8M0 scale (2^(e-127)); a
+// scale covers 32 consecutive elements along K (OCP Microscaling Formats
+// specification v1.0).  The page "[Feature] Introduce tile scheduler #2441"
+// lists an MXFP8 block-scaled persistent GEMM among its examples (PR overview,
+// changed files: blockscaled_gemm ... mxfp8 ... 1d1d) driven by the same tile
+// scheduler, without printing its layouts; the layout here is the plain "1d1d"
+// reading: A[M][K] and B[N][K] K-contiguous bytes, SFA[M][K/32] and
+// SFB[N][K/32] scale bytes, C[M][N] bf16, fp32 accumulation.
+//
+// Same structure as the fp16/bf16 kernel: persistent workers on one
+// `while valid()` loop over their tiles, a loader running one LDS stage ahead
+// with its own scheduler copy, buffer_load ... lds DMA with range-checked
+// descriptors (zero fill past the matrix), XOR-swizzled 16-byte LDS chunks.
+// Specific to this kernel:
+//   * math: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0 scale per
+//     operand row and 32-deep block); 4 waves in a 2x2 grid, each a 128x128
+//     sub-tile = 4x4 blocks of 32x32, all 256 AGPRs as accumulators;
+//   * tile 256x256, 128-deep slabs: a stage holds A and B (256 rows x 128
+//     bytes each) and their scale bytes (256 rows x 4 bytes each), 66 KiB;
+//     two stages;
+//   * operand layout of the instruction: lane l supplies row l%32; its bytes
+//     0-15 are k = 16*(l/32) + 0..15 of the 64-deep step and bytes 16-31 are
+//     k = 32 + 16*(l/32) + 0..15; lane l also supplies the scale of row l%32
+//     for the step's 32-deep block l/32.  A fragment is therefore two 16-byte
+//     LDS reads and a scale one LDS byte read (no register shuffling);
+//   * B is the instruction's first operand, so a lane's 16 results run along
+//     N.  Its rows are permuted (src row rho -> column pi(rho)) so that a lane
+//     holds two runs of 8 consecutive columns and the epilogue writes 16-byte
+//     pieces, 32 contiguous bytes per C row and store instruction.
+#pragma once
+
+#include "tile_scheduler.h"
+#include "tsgemm_device.h"
+
+namespace tsg {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+struct MxArgs {
+    const uint8_t* A;    // [M][K] E4M3
+    const uint8_t* SFA;  // [M][K/32] E8M0
+    const uint8_t* B;    // [N][K] E4M3
+    const uint8_t* SFB;  // [N][K/32] E8M0
+    uint16_t* C;         // [M][N] bf16
+    int32_t* trace;      // optional (worker, iter, m, n) per processed tile
+    int64_t M, N, K;
+    uint32_t m_blocks, n_blocks, k_blocks, group;
+    uint32_t P, max_iters, num_xcd;
+    uint32_t cluster, col_major;
+};
+
+// acc += src0 x src1 with per-row E8M0 scales (byte 0 of each scale
+// register, op_sel 0), both operands E4M3.  Accumulator constrained to AGPRs
+// as in the fp16/bf16 kernel.  The leading s_nop gives the two wait states an
+// MFMA needs after a VALU write of one of its source VGPRs: the compiler
+// zero-extends the scale bytes with VALU ops it may place right before this
+// asm, and it pads only instructions it knows to be MFMAs.
+__device__ __forceinline__ void mfma_mx32(f32x16& acc, i32x8 src0, i32x8 src1, uint32_t s0, uint32_t s1) {
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(acc) : "v"(src0), "v"(src1), "v"(s0), "v"(s1));
+}
+
+// One dword per lane from a buffer into LDS (M0 + 4 * lane).
+__device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                 : "memory");
+}
+
+struct MxTraits {
+    static constexpr int BM = 256, BN = 256, BK = 128, L = 2;
+    static constexpr int THREADS = 256;           // 4 waves, 2 x 2
+    static constexpr int WM = 128, WN = 128;      // wave sub-tile
+    static constexpr int F = 4;                   // 32x32 blocks per wave side
+    static constexpr int A_BYTES = BM * BK;       // 32 KiB
+    static constexpr int B_BYTES = BN * BK;       // 32 KiB
+    static constexpr int SA_OFF = A_BYTES + B_BYTES;
+    static constexpr int SB_OFF = SA_OFF + BM * 4;
+    static constexpr int STAGE = SB_OFF + BN * 4;  // 66 KiB
+    static constexpr int LDS = STAGE * L;
+    static constexpr int NA = A_BYTES / (1024 * 4);  // 16-byte DMAs per wave for A (8)
+    static constexpr int NB = B_BYTES / (1024 * 4);  // ... for B (8)
+    static constexpr int NL = NA + NB + 2;           // + one scale dword DMA each for SFA, SFB
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(BM / 4 == 64 && BN / 4 == 64, "one scale DMA (64 rows) per wave and operand");
+};
+constexpr int kMxGap = 2;  // MFMAs (64 cycles each) between the last read of a fragment set and its refill
+
+// Column of B (within a 32-column block) that instruction row rho carries:
+// rho = 8j + 4h + t  ->  16*(j/2) + 8h + 4*(j%2) + t.  A lane of the result
+// with half h then holds columns 8h + 0..7 (values 0-7) and 16 + 8h + 0..7
+// (values 8-15).
+__device__ __forceinline__ uint32_t mx_col_of_row(uint32_t rho) {
+    return 16u * (rho >> 4) + 8u * ((rho >> 2) & 1u) + 4u * ((rho >> 3) & 1u) + (rho & 3u);
+}
+
+// Swizzled chunk slot of logical 16-byte chunk c in an LDS row: A rows use
+// row & 7.  B rows use bits 0, 1 and 3 of the row, which for row pi(rho) is
+// rho & 7: the 8 lanes of one read phase hit 8 distinct slots either way.
+__device__ __forceinline__ uint32_t mx_swz_b(uint32_t n) { return (n & 3u) | ((n >> 1) & 4u); }
+
+__global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
+    using T = MxTraits;
+    constexpr int F = T::F, NA = T::NA, NB = T::NB, NL = T::NL, L = T::L;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem);
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wr = wave >> 1, wc = wave & 1u;
+    const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K, KB = K / 32u;
+    const uint32_t k_blocks = args.k_blocks;
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
+
+    // ---- DMA source offsets (bytes from the slab origin) ----
+    // Instruction q of this wave fills 16-byte LDS positions p = (wave*NA + q)*64
+    // + lane: stage row p/8 = (wave*NA + q)*8 + lane/8, slot lane%8.  The lane
+    // fetches the logical chunk the swizzle puts at that slot.  A's swizzle is
+    // lane/8; B's also takes bit 3 of the row, i.e. the parity of q.
+    uint32_t voff[NL];
+    {
+        const uint32_t r8 = lane >> 3, slot = lane & 7u;
+#pragma unroll
+        for (int q = 0; q < NA; ++q)
+            voff[q] = (((wave * NA + q) * 8u + r8) * K) + ((slot ^ r8) * 16u);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const uint32_t row = (wave * NB + q) * 8u + r8;
+            voff[NA + q] = row * K + ((slot ^ mx_swz_b(row)) * 16u);
+        }
+        voff[NA + NB] = (wave * 64u + lane) * KB;      // SFA: this slab's 4 scale bytes of row wave*64+lane
+        voff[NA + NB + 1] = (wave * 64u + lane) * KB;  // SFB likewise
+    }
+
+    // ---- per-lane LDS read offsets (bytes from the stage origin) ----
+    // The instruction lane (h, r): operand row r, byte halves from chunks
+    // 4*ks + h (bytes 0-15) and 4*ks + 2 + h (bytes 16-31) of the 8-chunk row.
+    const uint32_t h = lane >> 5, r = lane & 31u;
+    const uint32_t a_row = wr * T::WM + r;                     // + 32*fm
+    const uint32_t b_row = wc * T::WN + mx_col_of_row(r);      // + 32*fn
+    uint32_t a_off[2][2], b_off[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t c = 4u * ks + 2u * j + h;
+            a_off[ks][j] = a_row * T::BK + ((c ^ (a_row & 7u)) * 16u);
+            b_off[ks][j] = T::A_BYTES + b_row * T::BK + ((c ^ mx_swz_b(b_row)) * 16u);
+        }
+    // scale byte of block 2*ks + h of the row
+    const uint32_t sa_off = T::SA_OFF + a_row * 4u + h, sb_off = T::SB_OFF + b_row * 4u + h;
+
+    // ---- loader: its own scheduler copy, L slabs ahead of the math ----
+    TileScheduler ld;
+    ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
+    ld.init(wid);
+    uint32_t ld_k = 0, ld_phase = 0;
+    i32x4 rs_a, rs_b, rs_sa, rs_sb;
+    uint32_t dma_lds = 0;
+
+    // Descriptors and LDS target of the loader's next slab, then advance it.
+    // Past the end the descriptors have zero range: the DMA then writes zeros
+    // into a stage nobody reads, so every slab issues the same instructions.
+    auto next_slab = [&]() __attribute__((always_inline)) {
+        dma_lds = lds_base + (ld_phase % L) * T::STAGE;
+        const bool live = k_blocks != 0 && ld.valid();
+        const int64_t m0 = live ? (int64_t)ld.m_idx * T::BM : 0, n0 = live ? (int64_t)ld.n_idx * T::BN : 0;
+        const int64_t k0 = (int64_t)ld_k * T::BK, kb0 = k0 / 32, kbs = args.K / 32;
+        const int64_t a_left = (args.M - m0) * args.K - k0, a_cap = (int64_t)T::BM * args.K;
+        const int64_t b_left = (args.N - n0) * args.K - k0, b_cap = (int64_t)T::BN * args.K;
+        const int64_t sa_left = (args.M - m0) * kbs - kb0, sa_cap = (int64_t)T::BM * kbs;
+        const int64_t sb_left = (args.N - n0) * kbs - kb0, sb_cap = (int64_t)T::BN * kbs;
+        rs_a = rsrc_words(args.A + (m0 * args.K + k0) * live, live ? (uint32_t)(a_left < a_cap ? a_left : a_cap) : 0u);
+        rs_b = rsrc_words(args.B + (n0 * args.K + k0) * live, live ? (uint32_t)(b_left < b_cap ? b_left : b_cap) : 0u);
+        rs_sa = rsrc_words(args.SFA + (m0 * kbs + kb0) * live, live ? (uint32_t)(sa_left < sa_cap ? sa_left : sa_cap) : 0u);
+        rs_sb = rsrc_words(args.SFB + (n0 * kbs + kb0) * live, live ? (uint32_t)(sb_left < sb_cap ? sb_left : sb_cap) : 0u);
+        if (live && ++ld_k == k_blocks) {
+            ld_k = 0;
+            ld.next_tile();
+        }
+        ++ld_phase;
+    };
+    // DMA q of a slab: the two scale dwords first, then A and B chunks
+    auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        if constexpr (q == 0)
+            dma4(dma_lds + T::SA_OFF + wave * 256u, voff[NA + NB], rs_sa);
+        else if constexpr (q == 1)
+            dma4(dma_lds + T::SB_OFF + wave * 256u, voff[NA + NB + 1], rs_sb);
+        else if constexpr (q - 2 < NA)
+            dma16(dma_lds + (wave * NA + (q - 2)) * 1024u, voff[q - 2], rs_a);
+        else
+            dma16(dma_lds + T::A_BYTES + (wave * NB + (q - 2 - NA)) * 1024u, voff[q - 2], rs_b);
+    };
+
+    // ---- fragments and scales: two register sets, the one this k-step's
+    // MFMAs read and the one the next k-step's LDS reads fill ----
+    f32x16 acc[F][F];
+#pragma unroll
+    for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn) acc[fm][fn] = f32x16{};
+    u32x4 fa[2][F][2], fb[2][F][2];
+    uint32_t sa[2][F], sb[2][F];
+
+    // per-k-step address registers: stage base folded in once, then
+    // register + immediate (32 rows = 4096 bytes of fragment, 128 of scales)
+    uint32_t ra[2], rb[2], rsa, rsb;
+    auto set_addr = [&](auto ks_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int KS = decltype(ks_c)::value;
+        ra[0] = lds_base + st + a_off[KS][0];
+        ra[1] = lds_base + st + a_off[KS][1];
+        rb[0] = lds_base + st + b_off[KS][0];
+        rb[1] = lds_base + st + b_off[KS][1];
+        rsa = lds_base + st + sa_off + 2u * KS;
+        rsb = lds_base + st + sb_off + 2u * KS;
+    };
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    // read op r in consumption order: units A0, B0..B3, A1..A3, each three
+    // reads (the two 16-byte halves, then the scale byte)
+    constexpr int R = 3 * 2 * F;
+    auto read_op = [&](auto set_c, auto r_c) __attribute__((always_inline)) {
+        constexpr int SET = decltype(set_c)::value, rr = decltype(r_c)::value;
+        constexpr int u = rr / 3, part = rr % 3;
+        constexpr bool is_a = (u == 0 || u > F);
+        constexpr int f = u == 0 ? 0 : (u > F ? u - F : u - 1);
+        if constexpr (is_a) {
+            if constexpr (part < 2)
+                fa[SET][f][part] = *(const lds_u32x4*)((lds_u8*)(uintptr_t)ra[part] + f * 32 * T::BK);
+            else
+                sa[SET][f] = *((const lds_u8*)(uintptr_t)rsa + f * 32 * 4);
+        } else {
+            if constexpr (part < 2)
+                fb[SET][f][part] = *(const lds_u32x4*)((lds_u8*)(uintptr_t)rb[part] + f * 32 * T::BK);
+            else
+                sb[SET][f] = *((const lds_u8*)(uintptr_t)rsb + f * 32 * 4);
+        }
+    };
+    auto read_all = [&](auto set_c, auto ks_c, uint32_t st) __attribute__((always_inline)) {
+        set_addr(ks_c, st);
+        static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, r_c); });
+    };
+
+    // One 64-deep k-step: 16 MFMAs (fm-major) from register set CUR, with the
+    // memory operations for what follows between them: the reads of the next
+    // k-step into set NXT and, in a slab's LAST k-step, the DMA of slab
+    // phase + L.  LAST first waits for the next slab and passes the workgroup
+    // barrier (after S0 MFMAs), then refills the stage just consumed and reads
+    // the next slab's first k-step; otherwise the reads take k-step KSN of the
+    // current stage.  No read into a set starts within kMxGap MFMAs of the
+    // last MFMA that read it.
+    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st) __attribute__((always_inline)) {
+        constexpr int CUR = decltype(cur_c)::value;
+        constexpr int NXT = 1 - CUR;
+        constexpr bool LAST = decltype(last_c)::value;
+        if constexpr (LAST) next_slab();
+        constexpr int NSTEP = F * F;
+        constexpr int S0 = LAST ? 2 : 0;
+        constexpr int START = S0 > kMxGap ? S0 : kMxGap;
+        constexpr int AVAIL = NSTEP - START - 1;
+        constexpr int D = LAST ? NL : 0;
+        constexpr int DPER = D ? (D + AVAIL - 1) / AVAIL : 0;
+        constexpr int PER = (R + AVAIL - 1) / AVAIL;
+        static_assert(AVAIL * PER >= R && (D == 0 || AVAIL * DPER >= D), "k-step too short for its memory operations");
+        if constexpr (!LAST) set_addr(ksn_c, read_st);
+        static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            constexpr int fm = s / F, fn = s % F;
+            const i32x8 b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            const i32x8 a8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fa[CUR][fm][0], fa[CUR][fm][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            mfma_mx32(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
+            if constexpr (LAST && s == S0 - 1) {
+                wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
+                lds_barrier();                                       // ... for every wave; stage phase free
+                set_addr(ksn_c, read_st);
+            }
+            if constexpr (s >= START) {
+                constexpr int i = s - START;
+                if constexpr (D) {
+                    constexpr int d0 = i * DPER;
+                    constexpr int d1 = d0 + DPER < D ? d0 + DPER : D;
+                    static_for<d0, d1>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+                }
+                constexpr int q0 = i * PER;
+                constexpr int q1 = q0 + PER < R ? q0 + PER : R;
+                static_for<q0, q1>([&](auto q_c) __attribute__((always_inline)) {
+                    read_op(std::integral_constant<int, NXT>{}, q_c);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using TRUE_ = std::integral_constant<bool, true>;
+    using FALSE_ = std::integral_constant<bool, false>;
+
+    // ---- epilogue: bf16 cast and store of one finished tile, then the k == 0
+    // clear.  Lane (h, r) of block (fm, fn) holds row 32*fm + r and columns
+    // 32*fn + 8h + 0..7 (values 0-7) and 32*fn + 16 + 8h + 0..7 (values 8-15).
+    TileScheduler sched;
+    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
+    const uint32_t row0 = wr * T::WM + r, col0 = wc * T::WN + 8u * h;
+    const uint32_t lane_off = (row0 * N + col0) * 2u;
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        gap_nops();  // the tile's last MFMAs have written their accumulators
+        const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
+        if (args.trace != nullptr && threadIdx.x == 0) {
+            int32_t* row = args.trace + 4 * ((size_t)wid * args.max_iters + sched.iter);
+            *(int4*)row = make_int4((int)wid, (int)sched.iter, (int)m_idx, (int)n_idx);
+            store_gap();
+        }
+        const int64_t m0 = (int64_t)m_idx * T::BM, n0 = (int64_t)n_idx * T::BN;
+        const uint32_t rows_left = (uint32_t)((args.M - m0) < T::BM ? (args.M - m0) : T::BM);
+        const uint32_t cols_left = (uint32_t)((args.N - n0) < T::BN ? (args.N - n0) : T::BN);
+        const uint32_t c_bytes = ((rows_left - 1u) * N + cols_left) * 2u;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(args.C + (m0 * args.N + n0), c_bytes);
+        static_for<0, F>([&](auto fm_c) __attribute__((always_inline)) {
+            constexpr int fm = decltype(fm_c)::value;
+            const bool row_ok = row0 + fm * 32 < rows_left;
+            static_for<0, F>([&](auto fn_c) __attribute__((always_inline)) {
+                constexpr int fn = decltype(fn_c)::value;
+                static_for<0, 2>([&](auto s_c) __attribute__((always_inline)) {
+                    constexpr int s = decltype(s_c)::value;
+                    const f32x16& x = acc[fm][fn];
+                    const u32x4 v = {cvt_pk<DT_BF16>(x[8 * s + 0], x[8 * s + 1]), cvt_pk<DT_BF16>(x[8 * s + 2], x[8 * s + 3]),
+                                     cvt_pk<DT_BF16>(x[8 * s + 4], x[8 * s + 5]), cvt_pk<DT_BF16>(x[8 * s + 6], x[8 * s + 7])};
+                    const bool ok = row_ok && col0 + 32u * fn + 16u * s < cols_left;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, (ok ? lane_off : 0x80000000u) + (fn * 32 + 16 * s) * 2,
+                                                           fm * 32 * N * 2, 0);
+                    store_gap();  // the store may still read its data registers
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                acc[fm][fn] = f32x16{};
+            });
+        });
+    };
+
+    // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
+    for (int s = 0; s < L; ++s) {
+        next_slab();
+        static_for<0, NL>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+    }
+    wait_vm<(L - 1) * NL < 63 ? (L - 1) * NL : 63>();
+    lds_barrier();
+    read_all(I0{}, I0{}, 0u);
+
+    // two k-steps per slab: set 0 then set 1; the second (LAST) publishes the
+    // next slab and reads its first k-step into set 0
+    uint32_t phase = 0;
+    for (sched.init(wid); sched.valid(); sched.next_tile()) {
+        for (uint32_t k = 0; k < k_blocks; ++k, ++phase) {
+            const uint32_t st_cur = (phase % L) * T::STAGE;
+            const uint32_t st_next = ((phase + 1u) % L) * T::STAGE;
+            kstep(I0{}, FALSE_{}, I1{}, st_cur);
+            kstep(I1{}, TRUE_{}, I0{}, st_next);
+        }
+        epilogue();
+    }
+    wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
+}
+
+}  // namespace tsg

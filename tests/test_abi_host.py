@@ -32,7 +32,11 @@ def test_library_exports_every_declared_function():
 
 
 @pytest.mark.parametrize("args,code,needle", [
-    ((512, 512, 512, 3, 128, 128, 64, 2, 2), tsg.EINVAL, "dtype"),
+    ((512, 512, 512, 4, 128, 128, 64, 2, 2), tsg.EINVAL, "dtype"),
+    ((512, 512, 512, 3, 256, 256, 64, 2, 2), tsg.EUNSUPPORTED, "MXFP8 tile"),
+    ((512, 512, 384 + 64, 3, 256, 256, 128, 2, 2), tsg.EINVAL, "multiple of block_K"),
+    ((512, 500, 512, 3, 256, 256, 128, 2, 2), tsg.EINVAL, "divisible by 8"),
+    ((512, 512, 1 << 23, 3, 256, 256, 128, 2, 2), tsg.EUNSUPPORTED, "exceeds 2^31"),
     ((-1, 512, 512, 1, 128, 128, 64, 2, 2), tsg.EINVAL, ">= 0"),
     ((512, 512, 500, 1, 128, 128, 64, 2, 2), tsg.EINVAL, "multiple of block_K"),
     ((512, 500, 512, 1, 128, 128, 64, 2, 2), tsg.EINVAL, "divisible by 8"),
@@ -48,6 +52,28 @@ def test_create_rejects(args, code, needle):
     h = lib.tsgemm_create(*args)
     assert not h
     assert needle in tsg.last_error()
+
+
+def test_mx_plan_info_and_dtype_mismatch():
+    """An MXFP8 plan: stage = A and B slabs (256 x 128 bytes each) plus 4 scale
+    bytes per row; tsgemm_run refuses it and tsgemm_run_mx refuses an fp16
+    plan, both before any HIP call."""
+    lib = tsg.load()
+    p = tsg.Plan(1000, 520, 384, "mxfp8", 256, 256, 128, 8, 3, num_workgroups=6)
+    inf = p.info()
+    assert (inf["dtype"], inf["lds_slots"], inf["stage_bytes"], inf["lds_bytes"]) == (3, 2, 67584, 135168)
+    assert (inf["m_blocks"], inf["n_blocks"], inf["k_blocks"], inf["waves"]) == (4, 3, 3, 2)
+    assert inf["threads_per_workgroup"] == 256
+    assert lib.tsgemm_run(p._h, None, None, None, None) == tsg.EINVAL
+    assert "tsgemm_run_mx" in tsg.last_error()
+    with pytest.raises(tsg.TsgemmError):
+        tsg.Plan(1000, 520, 384, "mxfp8", 256, 256, 128, 8, 2, waves=8)
+    q = tsg.Plan(512, 512, 512, "fp16", 128, 128, 64, 2, 2)
+    assert lib.tsgemm_run_mx(q._h, None, None, None, None, None, None) == tsg.EINVAL
+    assert "MXFP8" in tsg.last_error()
+    assert lib.tsgemm_run_mx_traced(p._h, None, None, None, None, None, None, None) == tsg.EINVAL
+    assert "trace" in tsg.last_error()
+    assert p.trace_rows() == 6 * 2
 
 
 def test_null_plan_calls_fail_cleanly():
