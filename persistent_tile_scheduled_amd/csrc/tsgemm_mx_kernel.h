@@ -20,8 +20,11 @@
 //     operand row and 32-deep block); 4 waves in a 2x2 grid, each a 128x128
 //     sub-tile = 4x4 blocks of 32x32, all 256 AGPRs as accumulators;
 //   * tile 256x256, 128-deep slabs: a stage holds A and B (256 rows x 128
-//     bytes each) and their scale bytes (256 rows x 4 bytes each), 66 KiB;
-//     two stages;
+//     bytes each), 64 KiB; two stages.  Scale bytes travel separately, once
+//     per group of SG slabs (4 * SG bytes per row: one 16-byte DMA lane per
+//     row and 4 slabs) into a two-entry scale ring: fetching them per slab
+//     (4 bytes from each of 256 rows, a cache line per lane) cost as much
+//     address-unit work as the A and B slabs themselves;
 //   * operand layout of the instruction: lane l supplies row l%32; its bytes
 //     0-15 are k = 16*(l/32) + 0..15 of the 64-deep step and bytes 16-31 are
 //     k = 32 + 16*(l/32) + 0..15; lane l also supplies the scale of row l%32
@@ -71,6 +74,9 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsr
                  : "memory");
 }
 
+#ifndef TSG_MX_SG
+#define TSG_MX_SG 4
+#endif
 struct MxTraits {
     static constexpr int BM = 256, BN = 256, BK = 128, L = 2;
     static constexpr int THREADS = 256;           // 4 waves, 2 x 2
@@ -78,17 +84,35 @@ struct MxTraits {
     static constexpr int F = 4;                   // 32x32 blocks per wave side
     static constexpr int A_BYTES = BM * BK;       // 32 KiB
     static constexpr int B_BYTES = BN * BK;       // 32 KiB
-    static constexpr int SA_OFF = A_BYTES + B_BYTES;
-    static constexpr int SB_OFF = SA_OFF + BM * 4;
-    static constexpr int STAGE = SB_OFF + BN * 4;  // 66 KiB
-    static constexpr int LDS = STAGE * L;
-    static constexpr int NA = A_BYTES / (1024 * 4);  // 16-byte DMAs per wave for A (8)
+    static constexpr int STAGE = A_BYTES + B_BYTES;  // 64 KiB
+    static constexpr int SG = TSG_MX_SG;          // slabs per scale group
+    static constexpr int SC_ROW = 4 * SG;         // scale bytes per row and group
+    static constexpr int SC_OFF = STAGE * L;      // scale ring after the stages
+    static constexpr int SC_B = BM * SC_ROW;      // B's part of a ring entry
+    static constexpr int SC_ENTRY = (BM + BN) * SC_ROW;
+    static constexpr int LDS = SC_OFF + 2 * SC_ENTRY;
+    static constexpr int NA = A_BYTES / (1024 * 4);  // 16-byte DMAs per wave and slab for A (8)
     static constexpr int NB = B_BYTES / (1024 * 4);  // ... for B (8)
-    static constexpr int NL = NA + NB + 2;           // + one scale dword DMA each for SFA, SFB
+    static constexpr int ND = NA + NB;
+    static constexpr int LPR = SG / 4;            // 16-byte DMA lanes per row and group
+    static constexpr int NS = LPR;                // scale DMAs per wave and operand and group (64 rows)
+    static constexpr int NSC = 2 * NS;
+    static_assert(SG == 4 || SG == 8, "scale group");
+    static_assert(L == 2, "the slabs' DMA counts vary (scale groups): every wait is for all of them");
     static_assert(LDS <= 160 * 1024, "LDS");
-    static_assert(BM / 4 == 64 && BN / 4 == 64, "one scale DMA (64 rows) per wave and operand");
+    static_assert(BM / 4 == 64 && BN / 4 == 64, "64 scale rows per wave and operand");
 };
-constexpr int kMxGap = 2;  // MFMAs (64 cycles each) between the last read of a fragment set and its refill
+#ifndef TSG_MX_GAP
+#define TSG_MX_GAP 2
+#endif
+#ifndef TSG_MX_S0
+#define TSG_MX_S0 2
+#endif
+#ifndef TSG_MX_SCALES_FIRST
+#define TSG_MX_SCALES_FIRST 1
+#endif
+constexpr int kMxGap = TSG_MX_GAP;  // MFMAs (64 cycles each) between the last read of a fragment set and its refill
+constexpr int kMxS0 = TSG_MX_S0;    // MFMAs a slab's last k-step issues before its wait and barrier
 
 // Column of B (within a 32-column block) that instruction row rho carries:
 // rho = 8j + 4h + t  ->  16*(j/2) + 8h + 4*(j%2) + t.  A lane of the result
@@ -98,14 +122,21 @@ __device__ __forceinline__ uint32_t mx_col_of_row(uint32_t rho) {
     return 16u * (rho >> 4) + 8u * ((rho >> 2) & 1u) + 4u * ((rho >> 3) & 1u) + (rho & 3u);
 }
 
-// Swizzled chunk slot of logical 16-byte chunk c in an LDS row: A rows use
-// row & 7.  B rows use bits 0, 1 and 3 of the row, which for row pi(rho) is
-// rho & 7: the 8 lanes of one read phase hit 8 distinct slots either way.
-__device__ __forceinline__ uint32_t mx_swz_b(uint32_t n) { return (n & 3u) | ((n >> 1) & 4u); }
+// Swizzled slot of logical 16-byte chunk c in an LDS row is c ^ swz(row).
+// A fragment read has lanes 0-31 on 32 consecutive rows (B: rows pi(rho))
+// at one chunk and lanes 32-63 on the same rows at the next chunk.  On
+// gfx950 such a 16-byte-per-lane read is conflict-free only if, besides rows
+// 0-7 spreading over the 8 slots, rows r and r + 8 also land on different
+// slots (measured with the LDS bank-conflict counter: row & 7 alone costs a
+// 2-way conflict on every read).  A rows therefore use (row & 7) ^ bit 3 of
+// the row; B rows the same function of rho, i.e. bits 0, 1, 3 of the column
+// with bit 2 folded in.
+__device__ __forceinline__ uint32_t mx_swz_a(uint32_t m) { return (m & 7u) ^ ((m >> 3) & 1u); }
+__device__ __forceinline__ uint32_t mx_swz_b(uint32_t n) { return ((n & 3u) | ((n >> 1) & 4u)) ^ ((n >> 2) & 1u); }
 
 __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     using T = MxTraits;
-    constexpr int F = T::F, NA = T::NA, NB = T::NB, NL = T::NL, L = T::L;
+    constexpr int F = T::F, NA = T::NA, NB = T::NB, ND = T::ND, NS = T::NS, NSC = T::NSC, L = T::L;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
     const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem);
 
@@ -119,21 +150,26 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     // ---- DMA source offsets (bytes from the slab origin) ----
     // Instruction q of this wave fills 16-byte LDS positions p = (wave*NA + q)*64
     // + lane: stage row p/8 = (wave*NA + q)*8 + lane/8, slot lane%8.  The lane
-    // fetches the logical chunk the swizzle puts at that slot.  A's swizzle is
-    // lane/8; B's also takes bit 3 of the row, i.e. the parity of q.
-    uint32_t voff[NL];
+    // fetches the logical chunk the swizzle puts at that slot (a function of
+    // lane/8 and, through bit 3 of the row, of the parity of q).
+    uint32_t voff[ND + NS];
     {
         const uint32_t r8 = lane >> 3, slot = lane & 7u;
 #pragma unroll
-        for (int q = 0; q < NA; ++q)
-            voff[q] = (((wave * NA + q) * 8u + r8) * K) + ((slot ^ r8) * 16u);
+        for (int q = 0; q < NA; ++q) {
+            const uint32_t row = (wave * NA + q) * 8u + r8;
+            voff[q] = row * K + ((slot ^ mx_swz_a(row)) * 16u);
+        }
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const uint32_t row = (wave * NB + q) * 8u + r8;
             voff[NA + q] = row * K + ((slot ^ mx_swz_b(row)) * 16u);
         }
-        voff[NA + NB] = (wave * 64u + lane) * KB;      // SFA: this slab's 4 scale bytes of row wave*64+lane
-        voff[NA + NB + 1] = (wave * 64u + lane) * KB;  // SFB likewise
+        // scale instruction i: rows wave*64 + i*64/LPR + lane/LPR, 16-byte part
+        // lane%LPR of the group's 4*SG bytes (same offsets for SFA and SFB)
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            voff[ND + i] = (wave * 64u + i * (64u / T::LPR) + lane / T::LPR) * KB + (lane % T::LPR) * 16u;
     }
 
     // ---- per-lane LDS read offsets (bytes from the stage origin) ----
@@ -148,26 +184,33 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t c = 4u * ks + 2u * j + h;
-            a_off[ks][j] = a_row * T::BK + ((c ^ (a_row & 7u)) * 16u);
+            a_off[ks][j] = a_row * T::BK + ((c ^ mx_swz_a(a_row)) * 16u);
             b_off[ks][j] = T::A_BYTES + b_row * T::BK + ((c ^ mx_swz_b(b_row)) * 16u);
         }
-    // scale byte of block 2*ks + h of the row
-    const uint32_t sa_off = T::SA_OFF + a_row * 4u + h, sb_off = T::SB_OFF + b_row * 4u + h;
+    // scale byte of block 2*ks + h of the row, from the ring entry's record of
+    // the row (4 bytes per slab of the group)
+    const uint32_t sa_off = a_row * T::SC_ROW + h, sb_off = T::SC_B + b_row * T::SC_ROW + h;
 
     // ---- loader: its own scheduler copy, L slabs ahead of the math ----
     TileScheduler ld;
     ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     ld.init(wid);
-    uint32_t ld_k = 0, ld_phase = 0;
+    uint32_t ld_k = 0, ld_phase = 0, ld_grp = 0;
     i32x4 rs_a, rs_b, rs_sa, rs_sb;
-    uint32_t dma_lds = 0;
+    uint32_t dma_lds = 0, sc_lds = 0;
+    bool sc_issue = false;
 
-    // Descriptors and LDS target of the loader's next slab, then advance it.
+    // Descriptors and LDS targets of the loader's next slab, then advance it.
     // Past the end the descriptors have zero range: the DMA then writes zeros
-    // into a stage nobody reads, so every slab issues the same instructions.
+    // into a stage nobody reads, so every slab issues the same data DMAs.  A
+    // slab that starts a scale group (k % SG == 0) also fetches the group's
+    // scales into ring entry (group count) % 2.
     auto next_slab = [&]() __attribute__((always_inline)) {
         dma_lds = lds_base + (ld_phase % L) * T::STAGE;
         const bool live = k_blocks != 0 && ld.valid();
+        sc_issue = live && (ld_k % T::SG) == 0;
+        sc_lds = lds_base + T::SC_OFF + (ld_grp & 1u) * T::SC_ENTRY + wave * 64u * T::SC_ROW;
+        ld_grp += sc_issue ? 1u : 0u;
         const int64_t m0 = live ? (int64_t)ld.m_idx * T::BM : 0, n0 = live ? (int64_t)ld.n_idx * T::BN : 0;
         const int64_t k0 = (int64_t)ld_k * T::BK, kb0 = k0 / 32, kbs = args.K / 32;
         const int64_t a_left = (args.M - m0) * args.K - k0, a_cap = (int64_t)T::BM * args.K;
@@ -184,17 +227,19 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         }
         ++ld_phase;
     };
-    // DMA q of a slab: the two scale dwords first, then A and B chunks
+    // DMA q of a slab: the group's scale DMAs first (SFA then SFB, only when
+    // the slab starts a group), then A and B chunks
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int q = decltype(q_c)::value;
-        if constexpr (q == 0)
-            dma4(dma_lds + T::SA_OFF + wave * 256u, voff[NA + NB], rs_sa);
-        else if constexpr (q == 1)
-            dma4(dma_lds + T::SB_OFF + wave * 256u, voff[NA + NB + 1], rs_sb);
-        else if constexpr (q - 2 < NA)
-            dma16(dma_lds + (wave * NA + (q - 2)) * 1024u, voff[q - 2], rs_a);
-        else
-            dma16(dma_lds + T::A_BYTES + (wave * NB + (q - 2 - NA)) * 1024u, voff[q - 2], rs_b);
+        if constexpr (q < NSC) {
+            constexpr int i = q % NS;
+            if (sc_issue)
+                dma16(sc_lds + (q < NS ? 0u : (uint32_t)T::SC_B) + i * 1024u, voff[ND + i], q < NS ? rs_sa : rs_sb);
+        } else if constexpr (q - NSC < NA) {
+            dma16(dma_lds + (wave * NA + (q - NSC)) * 1024u, voff[q - NSC], rs_a);
+        } else {
+            dma16(dma_lds + T::A_BYTES + (wave * NB + (q - NSC - NA)) * 1024u, voff[q - NSC], rs_b);
+        }
     };
 
     // ---- fragments and scales: two register sets, the one this k-step's
@@ -207,42 +252,47 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     u32x4 fa[2][F][2], fb[2][F][2];
     uint32_t sa[2][F], sb[2][F];
 
-    // per-k-step address registers: stage base folded in once, then
-    // register + immediate (32 rows = 4096 bytes of fragment, 128 of scales)
+    // per-k-step address registers: stage and scale-record bases folded in
+    // once, then register + immediate (32 rows = 4096 bytes of fragment,
+    // 32 * SC_ROW of scales).  scb = scale ring entry + 4 * (slab in group).
     uint32_t ra[2], rb[2], rsa, rsb;
-    auto set_addr = [&](auto ks_c, uint32_t st) __attribute__((always_inline)) {
+    auto set_addr = [&](auto ks_c, uint32_t st, uint32_t scb) __attribute__((always_inline)) {
         constexpr int KS = decltype(ks_c)::value;
         ra[0] = lds_base + st + a_off[KS][0];
         ra[1] = lds_base + st + a_off[KS][1];
         rb[0] = lds_base + st + b_off[KS][0];
         rb[1] = lds_base + st + b_off[KS][1];
-        rsa = lds_base + st + sa_off + 2u * KS;
-        rsb = lds_base + st + sb_off + 2u * KS;
+        rsa = lds_base + scb + sa_off + 2u * KS;
+        rsb = lds_base + scb + sb_off + 2u * KS;
     };
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
     typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-    // read op r in consumption order: units A0, B0..B3, A1..A3, each three
-    // reads (the two 16-byte halves, then the scale byte)
+    // read op r in consumption order of units A0, B0..B3, A1..A3: with
+    // TSG_MX_SCALES_FIRST the eight scale bytes first, then the two 16-byte
+    // halves of every unit (the compiler zero-extends the scale bytes at the
+    // top of the consuming k-step, so they should be the first reads to land);
+    // otherwise unit by unit, halves then scale byte.
     constexpr int R = 3 * 2 * F;
     auto read_op = [&](auto set_c, auto r_c) __attribute__((always_inline)) {
         constexpr int SET = decltype(set_c)::value, rr = decltype(r_c)::value;
-        constexpr int u = rr / 3, part = rr % 3;
+        constexpr int u = TSG_MX_SCALES_FIRST ? (rr < 2 * F ? rr : (rr - 2 * F) / 2) : rr / 3;
+        constexpr int part = TSG_MX_SCALES_FIRST ? (rr < 2 * F ? 2 : (rr - 2 * F) % 2) : rr % 3;
         constexpr bool is_a = (u == 0 || u > F);
         constexpr int f = u == 0 ? 0 : (u > F ? u - F : u - 1);
         if constexpr (is_a) {
             if constexpr (part < 2)
                 fa[SET][f][part] = *(const lds_u32x4*)((lds_u8*)(uintptr_t)ra[part] + f * 32 * T::BK);
             else
-                sa[SET][f] = *((const lds_u8*)(uintptr_t)rsa + f * 32 * 4);
+                sa[SET][f] = *((const lds_u8*)(uintptr_t)rsa + f * 32 * T::SC_ROW);
         } else {
             if constexpr (part < 2)
                 fb[SET][f][part] = *(const lds_u32x4*)((lds_u8*)(uintptr_t)rb[part] + f * 32 * T::BK);
             else
-                sb[SET][f] = *((const lds_u8*)(uintptr_t)rsb + f * 32 * 4);
+                sb[SET][f] = *((const lds_u8*)(uintptr_t)rsb + f * 32 * T::SC_ROW);
         }
     };
-    auto read_all = [&](auto set_c, auto ks_c, uint32_t st) __attribute__((always_inline)) {
-        set_addr(ks_c, st);
+    auto read_all = [&](auto set_c, auto ks_c, uint32_t st, uint32_t scb) __attribute__((always_inline)) {
+        set_addr(ks_c, st, scb);
         static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, r_c); });
     };
 
@@ -254,20 +304,20 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     // the next slab's first k-step; otherwise the reads take k-step KSN of the
     // current stage.  No read into a set starts within kMxGap MFMAs of the
     // last MFMA that read it.
-    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st) __attribute__((always_inline)) {
+    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, uint32_t read_scb) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int NXT = 1 - CUR;
         constexpr bool LAST = decltype(last_c)::value;
         if constexpr (LAST) next_slab();
         constexpr int NSTEP = F * F;
-        constexpr int S0 = LAST ? 2 : 0;
+        constexpr int S0 = LAST ? kMxS0 : 0;
         constexpr int START = S0 > kMxGap ? S0 : kMxGap;
         constexpr int AVAIL = NSTEP - START - 1;
-        constexpr int D = LAST ? NL : 0;
+        constexpr int D = LAST ? NSC + ND : 0;
         constexpr int DPER = D ? (D + AVAIL - 1) / AVAIL : 0;
         constexpr int PER = (R + AVAIL - 1) / AVAIL;
         static_assert(AVAIL * PER >= R && (D == 0 || AVAIL * DPER >= D), "k-step too short for its memory operations");
-        if constexpr (!LAST) set_addr(ksn_c, read_st);
+        if constexpr (!LAST) set_addr(ksn_c, read_st, read_scb);
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / F, fn = s % F;
@@ -275,9 +325,9 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
             const i32x8 a8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fa[CUR][fm][0], fa[CUR][fm][1], 0, 1, 2, 3, 4, 5, 6, 7));
             mfma_mx32(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
             if constexpr (LAST && s == S0 - 1) {
-                wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
-                lds_barrier();                                       // ... for every wave; stage phase free
-                set_addr(ksn_c, read_st);
+                wait_vm<0>();    // slab phase+1 (and its scale group) has landed
+                lds_barrier();   // ... for every wave; stage phase and scale entries read are free
+                set_addr(ksn_c, read_st, read_scb);
             }
             if constexpr (s >= START) {
                 constexpr int i = s - START;
@@ -345,21 +395,28 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
     for (int s = 0; s < L; ++s) {
         next_slab();
-        static_for<0, NL>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+        static_for<0, NSC + ND>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
     }
-    wait_vm<(L - 1) * NL < 63 ? (L - 1) * NL : 63>();
+    wait_vm<0>();
     lds_barrier();
-    read_all(I0{}, I0{}, 0u);
+    auto scale_base = [&](uint32_t grp, uint32_t sub) __attribute__((always_inline)) -> uint32_t {
+        return T::SC_OFF + (grp & 1u) * T::SC_ENTRY + sub * 4u;
+    };
+    read_all(I0{}, I0{}, 0u, scale_base(0u, 0u));
 
     // two k-steps per slab: set 0 then set 1; the second (LAST) publishes the
-    // next slab and reads its first k-step into set 0
-    uint32_t phase = 0;
+    // next slab and reads its first k-step into set 0.  grp counts the scale
+    // groups consumed so far exactly as the loader counts those it fetched.
+    uint32_t phase = 0, grp = 0;
     for (sched.init(wid); sched.valid(); sched.next_tile()) {
         for (uint32_t k = 0; k < k_blocks; ++k, ++phase) {
             const uint32_t st_cur = (phase % L) * T::STAGE;
             const uint32_t st_next = ((phase + 1u) % L) * T::STAGE;
-            kstep(I0{}, FALSE_{}, I1{}, st_cur);
-            kstep(I1{}, TRUE_{}, I0{}, st_next);
+            const uint32_t k_next = k + 1u < k_blocks ? k + 1u : 0u;   // next slab's k (next tile at the end)
+            const uint32_t grp_next = grp + ((k_next % T::SG) == 0u ? 1u : 0u);
+            kstep(I0{}, FALSE_{}, I1{}, st_cur, scale_base(grp, k % T::SG));
+            kstep(I1{}, TRUE_{}, I0{}, st_next, scale_base(grp_next, k_next % T::SG));
+            grp = grp_next;
         }
         epilogue();
     }
