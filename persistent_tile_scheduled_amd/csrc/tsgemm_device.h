@@ -28,6 +28,9 @@ enum { DT_FP16 = 1, DT_BF16 = 2 };
 #define TSG_DMA_SPACING 3
 #endif
 constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA issues
+#ifndef TSG_DMA_FIRST
+#define TSG_DMA_FIRST 12  // DMAs per slab issued in its first k-step of issue (0: all)
+#endif
 #ifndef TSG_GAP
 #define TSG_GAP 4
 #endif

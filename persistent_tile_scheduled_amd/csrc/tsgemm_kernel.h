@@ -56,6 +56,9 @@ struct GemmTraits {
     static constexpr int NA = A_BYTES / (1024 * NW);        // DMA instructions per wave, A
     static constexpr int NB = B_BYTES / (1024 * NW);        // DMA instructions per wave, B
     static constexpr int NL = NA + NB;
+    // DMAs of a slab issued in the LAST k-step of the slab two back; with two
+    // k-steps per slab the remaining NL - DF go out during the next k-step
+    static constexpr int DF = (BK == 64 && TSG_DMA_FIRST > 0 && TSG_DMA_FIRST < NL) ? TSG_DMA_FIRST : NL;
     static_assert(BK == 32 || BK == 64, "block_K");
     static_assert(FN % 2 == 0 && FM >= 1, "wave tile");
     static_assert(NA >= 1 && NB >= 1 && NA * 1024 * NW == A_BYTES && NB * 1024 * NW == B_BYTES,
@@ -238,7 +241,10 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int START = S0 > kGap ? S0 : kGap;       // first step with memory operations
         constexpr int AVAIL = NSTEP - START - 1;
         static_assert(AVAIL >= 2, "k-step too short for its memory operations");
-        constexpr int D = LAST ? NL : 0;
+        // LAST issues DMAs [0, DF) of slab phase+L; the following first k-step
+        // of the next slab issues [DF, NL) of the same slab
+        constexpr int D = LAST ? T::DF : (SAME ? 0 : NL - T::DF);
+        constexpr int D0 = LAST ? 0 : T::DF;
         // DMA issues are spaced DS MFMAs apart: a burst of them right after the
         // barrier would overflow the texture unit's queue and stall issue
         constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             }
             if constexpr (s >= START) {
                 constexpr int i = s - START;
-                if constexpr (D && i % DS == 0 && i / DS < D) dma_op(std::integral_constant<int, i / DS>{});
+                if constexpr (D && i % DS == 0 && i / DS < D) dma_op(std::integral_constant<int, D0 + i / DS>{});
                 constexpr int q0 = i * PER;
                 constexpr int q1 = q0 + PER < QR ? q0 + PER : QR;
                 static_for<q0, q1>([&](auto q_c) __attribute__((always_inline)) {
@@ -323,12 +329,16 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         });
     };
 
-    // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
+    // prologue: slabs 0..L-1 in flight (the last one's DMAs [DF, NL) follow in
+    // the first k-step), the first k-step's fragments read
     for (int s = 0; s < L; ++s) {
         next_slab();
-        static_for<0, NL>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+        if (s + 1 < L)
+            static_for<0, NL>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+        else
+            static_for<0, T::DF>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
     }
-    wait_vm<(L - 1) * NL < 63 ? (L - 1) * NL : 63>();
+    wait_vm<(L - 2) * NL + T::DF < 63 ? (L - 2) * NL + T::DF : 63>();
     lds_barrier();
     read_all(I0{}, I0{}, 0u);
 

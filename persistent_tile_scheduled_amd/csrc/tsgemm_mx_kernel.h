@@ -77,6 +77,9 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsr
 #ifndef TSG_MX_SG
 #define TSG_MX_SG 4
 #endif
+#ifndef TSG_MX_SCALES_LAST
+#define TSG_MX_SCALES_LAST 1
+#endif
 struct MxTraits {
     static constexpr int BM = 256, BN = 256, BK = 128, L = 2;
     static constexpr int THREADS = 256;           // 4 waves, 2 x 2
@@ -227,10 +230,12 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         }
         ++ld_phase;
     };
-    // DMA q of a slab: the group's scale DMAs first (SFA then SFB, only when
-    // the slab starts a group), then A and B chunks
+    // DMA q of a slab: A and B chunks, then (only when the slab starts a
+    // scale group) the group's scale DMAs, SFA then SFB -- with TSG_MX_SCALES_LAST
+    // 0 the scale DMAs come first instead.
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
-        constexpr int q = decltype(q_c)::value;
+        constexpr int qq = decltype(q_c)::value;
+        constexpr int q = TSG_MX_SCALES_LAST ? (qq < ND ? qq + NSC : qq - ND) : qq;
         if constexpr (q < NSC) {
             constexpr int i = q % NS;
             if (sc_issue)
