@@ -13,8 +13,10 @@ Prints one JSON line:
   cpu_baseline  the CPU oracle (fp64 triple loop) timed on this host on a
              bounded sample of the same product (its first R rows of C)
 --workload picks another of the six shapes, or the block-scaled FP8 shape
-mx_8192_mxfp8 (tsgemm_run_mx: E4M3 elements with E8M0 scales per 32 along K,
-bf16 output; roofline against the dense fp8 MFMA peak; cpu_baseline the MX
+mx_8192_mxfp8 (E4M3 elements with E8M0 scales per 32 along K, bf16 output;
+one step = tsgemm_mx_pack_scales of SFA and of SFB from their row-major layout
+plus tsgemm_run_mx_packed, or with --mx-scales rowmajor tsgemm_run_mx alone;
+roofline: the GEMM kernel against the dense fp8 MFMA peak; cpu_baseline the MX
 oracle; context torch's per-tensor-scaled fp8 product when available).  --cold
 rewrites a 512 MiB buffer before every timed launch so the small shapes are not
 served from the Infinity Cache.
@@ -193,6 +195,8 @@ def main():
                     help="rewrite a 512 MiB scratch buffer before every timed launch (caches cold); "
                          "the per-launch events still bracket only the GEMM")
     ap.add_argument("--no-torch-context", action="store_true")
+    ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
+                    help="MX workload: pack the scales on the device each step (default) or feed them row-major")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -227,11 +231,25 @@ def main():
     P = plan.num_workgroups
     stream = torch.cuda.current_stream(dev)
 
-    def launch():
-        if mx:
+    packed = mx and args.mx_scales == "packed"
+    if packed:
+        sfp = [torch.empty((plan.mx_packed_scale_bytes(op),), dtype=torch.uint8, device=dev) for op in (0, 1)]
+
+    def launch(gemm_start=None, gemm_end=None):
+        # the events bracket the GEMM kernel alone (the roofline's kernel time)
+        if packed:
+            plan.mx_pack_scales(operands[1], sfp[0], 0, stream)
+            plan.mx_pack_scales(operands[3], sfp[1], 1, stream)
+        if gemm_start is not None:
+            gemm_start.record(stream)
+        if packed:
+            plan.run_mx_packed(operands[0], sfp[0], operands[2], sfp[1], C, stream)
+        elif mx:
             plan.run_mx(*operands, C, stream)
         else:
             plan.run(Ad, Bd, C, stream)
+        if gemm_end is not None:
+            gemm_end.record(stream)
 
     for _ in range(args.warmup):
         launch()
@@ -245,15 +263,14 @@ def main():
     for i in range(args.steps):
         if scratch is not None:
             scratch.fill_(i & 0xFF)
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
+        launch(starts[i], ends[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     mean_ms = sum(launch_ms) / len(launch_ms)
     if scratch is not None:
         # wall time includes the cache flushes: report the GEMM launches only
+        # (and, for packed MX scales, not the packing either)
         wall = sum(launch_ms) * 1e-3
 
     flops = float(w.flops)
@@ -281,6 +298,8 @@ def main():
             "num_stages": w.num_stages, "lds_slots": info["lds_slots"], "num_workgroups": P,
             "inputs": (f"normal(0,1) MX-encoded (E4M3 + E8M0 per 32 along K), seed {w.seed}" if mx
                        else f"{w.dist}, seed {w.seed}"),
+            **({"scales": ("row-major, packed on the device inside every step" if packed else "row-major")}
+               if mx else {}),
         },
         "roofline": {
             "bound": "mfma",

@@ -164,6 +164,28 @@ int tsgemm_run_mx(const tsgemm_plan* plan, const void* A, const void* SFA, const
 int tsgemm_run_mx_traced(const tsgemm_plan* plan, const void* A, const void* SFA, const void* B,
                          const void* SFB, void* C, void* stream, int32_t* trace);
 
+/* Tile-blocked scale layout for tsgemm_run_mx_packed.  The row-major SFA/SFB
+ * above make every lane of the kernel's scale fetch touch its own cache line
+ * (one row each); the packed layout puts each tile's scales for a group of 4
+ * slabs (512 elements of K) in one contiguous 4 KiB block:
+ *   SFP[block][group][256][16]: block = 256-row block of A (operand 0) or of
+ *   B's N rows (operand 1), group = g covers K blocks 16g .. 16g+15, row r of
+ *   the block, byte j = SF[block*256 + r][16g + j]; rows past M (N) and bytes
+ *   past K/32 are 0.
+ * tsgemm_mx_packed_scale_bytes: bytes of SFP for `operand`
+ *   (= blocks * ceil(k_blocks / 4) * 4096; 0 when K == 0), < 0 on error.
+ * tsgemm_mx_pack_scales: writes SFP from SF (DEVICE pointers: SF 4-byte, SFP
+ *   16-byte aligned, SFP holding tsgemm_mx_packed_scale_bytes bytes) on
+ *   `stream`; a pure data permutation.
+ * tsgemm_run_mx_packed: tsgemm_run_mx with packed SFA and SFB (16-byte
+ *   aligned); C is bit for bit the result of tsgemm_run_mx on the unpacked
+ *   scales.  For callers whose scale producer can write the packed layout, or
+ *   who pack static (weight) scales once. */
+int64_t tsgemm_mx_packed_scale_bytes(const tsgemm_plan* plan, int operand);
+int tsgemm_mx_pack_scales(const tsgemm_plan* plan, int operand, const void* SF, void* SFP, void* stream);
+int tsgemm_run_mx_packed(const tsgemm_plan* plan, const void* A, const void* SFAP, const void* B,
+                         const void* SFBP, void* C, void* stream);
+
 int64_t tsgemm_num_tiles(const tsgemm_plan* plan);       /* < 0 on error                */
 int tsgemm_num_workgroups(const tsgemm_plan* plan);      /* resolves the default P      */
 int tsgemm_plan_info(const tsgemm_plan* plan, tsgemm_info* info);

@@ -31,7 +31,8 @@ OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, -1, -2, -3, -4
 EXPORTS = (
     "tsgemm_create", "tsgemm_set_num_workgroups", "tsgemm_set_waves", "tsgemm_set_schedule",
     "tsgemm_set_xcd_remap", "tsgemm_run",
-    "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
+    "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_mx_packed_scale_bytes",
+    "tsgemm_mx_pack_scales", "tsgemm_run_mx_packed", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
 )
 
@@ -93,6 +94,12 @@ def load(path: str | None = None):
     lib.tsgemm_run_mx.restype = i32
     lib.tsgemm_run_mx_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.tsgemm_run_mx_traced.restype = i32
+    lib.tsgemm_mx_packed_scale_bytes.argtypes = [vp, i32]
+    lib.tsgemm_mx_packed_scale_bytes.restype = i64
+    lib.tsgemm_mx_pack_scales.argtypes = [vp, i32, vp, vp, vp]
+    lib.tsgemm_mx_pack_scales.restype = i32
+    lib.tsgemm_run_mx_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.tsgemm_run_mx_packed.restype = i32
     lib.tsgemm_num_tiles.argtypes = [vp]
     lib.tsgemm_num_tiles.restype = i64
     lib.tsgemm_num_workgroups.argtypes = [vp]
@@ -251,6 +258,42 @@ class Plan:
         a, sa, b, sb, c = self._mx_args(A, SFA, B, SFB, C)
         s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
         _check(self._lib.tsgemm_run_mx(self._h, a, sa, b, sb, c, s))
+
+    def mx_packed_scale_bytes(self, operand: int) -> int:
+        """Bytes of the packed scale array of operand 0 (SFA) or 1 (SFB)."""
+        return _check(self._lib.tsgemm_mx_packed_scale_bytes(self._h, operand))
+
+    def mx_pack_scales(self, SF, SFP, operand: int, stream=None) -> None:
+        """tsgemm_mx_pack_scales: SF [rows, K/32] (1-byte, CUDA) -> SFP (1-byte CUDA tensor of
+        mx_packed_scale_bytes(operand) bytes)."""
+        import torch
+        rows = self.M if operand == 0 else self.N
+        if SF.element_size() != 1 or tuple(SF.shape) != (rows, self.K // 32) or not SF.is_contiguous() \
+                or not SF.is_cuda:
+            raise ValueError(f"SF must be a contiguous 1-byte CUDA tensor of shape {(rows, self.K // 32)}")
+        need = self.mx_packed_scale_bytes(operand)
+        if SFP.element_size() != 1 or SFP.numel() != need or not SFP.is_contiguous() or not SFP.is_cuda:
+            raise ValueError(f"SFP must be a contiguous 1-byte CUDA tensor of {need} bytes")
+        s = (stream or torch.cuda.current_stream(SFP.device)).cuda_stream
+        _check(self._lib.tsgemm_mx_pack_scales(self._h, operand, SF.data_ptr(), SFP.data_ptr(), s))
+
+    def run_mx_packed(self, A, SFAP, B, SFBP, C, stream=None) -> None:
+        """tsgemm_run_mx_packed: as run_mx with scales from mx_pack_scales."""
+        import torch
+        if self.dtype != MXFP8:
+            raise ValueError("run_mx_packed needs a plan created with dtype 'mxfp8'")
+        for name, t, shape in (("A", A, (self.M, self.K)), ("B", B, (self.N, self.K))):
+            if t.element_size() != 1 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous 1-byte CUDA tensor of shape {shape}")
+        for name, t, op in (("SFAP", SFAP, 0), ("SFBP", SFBP, 1)):
+            need = self.mx_packed_scale_bytes(op)
+            if t.element_size() != 1 or t.numel() != need or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous 1-byte CUDA tensor of {need} bytes")
+        if C.dtype != torch.bfloat16 or tuple(C.shape) != (self.M, self.N) or not C.is_contiguous() or not C.is_cuda:
+            raise ValueError(f"C must be a contiguous torch.bfloat16 CUDA tensor of shape {(self.M, self.N)}")
+        s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        _check(self._lib.tsgemm_run_mx_packed(self._h, A.data_ptr(), SFAP.data_ptr(), B.data_ptr(),
+                                              SFBP.data_ptr(), C.data_ptr(), s))
 
     def run_mx_traced(self, A, SFA, B, SFB, C, trace, stream=None) -> None:
         import torch

@@ -198,8 +198,17 @@ int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* 
     return TSGEMM_OK;
 }
 
+// Scale groups per tile column of K (SG slabs each) and bytes of one packed
+// scale array for `blocks` row (or column) blocks.
+uint32_t mx_groups(const tsgemm_plan* p) {
+    return (uint32_t)((p->k_blocks + tsg::MxTraits::SG - 1) / tsg::MxTraits::SG);
+}
+int64_t mx_packed_bytes(const tsgemm_plan* p, int64_t blocks) {
+    return blocks * (int64_t)mx_groups(p) * tsg::MxTraits::BM * tsg::MxTraits::SC_ROW;
+}
+
 int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB, void* C,
-                void* stream, int32_t* trace) {
+                void* stream, int32_t* trace, bool packed) {
     g_err[0] = '\0';
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (!is_mx(p)) return fail(TSGEMM_EINVAL, "tsgemm_run_mx needs a TSGEMM_MXFP8 plan (dtype %d)", p->dtype);
@@ -208,8 +217,9 @@ int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void
     if (p->K > 0 && (!A || !B || !SFA || !SFB)) return fail(TSGEMM_EINVAL, "A, SFA, B or SFB is NULL");
     if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) | reinterpret_cast<uintptr_t>(C)) & 15u)
         return fail(TSGEMM_EINVAL, "A, B and C must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)
-        return fail(TSGEMM_EINVAL, "SFA and SFB must be 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & (packed ? 15u : 3u))
+        return fail(TSGEMM_EINVAL, packed ? "packed SFA and SFB must be 16-byte aligned"
+                                          : "SFA and SFB must be 4-byte aligned");
     Grid g;
     int rc = resolve_grid(p, &g);
     if (rc != TSGEMM_OK) return rc;
@@ -239,8 +249,13 @@ int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void
         a.num_xcd = g.xcds;
         a.cluster = (uint32_t)p->cluster;
         a.col_major = (uint32_t)p->col_major;
-        hipLaunchKernelGGL(tsg::tsgemm_mx_kernel, dim3(g.P), dim3(tsg::MxTraits::THREADS), 0,
-                           static_cast<hipStream_t>(stream), a);
+        a.n_groups = mx_groups(p);
+        if (packed)
+            hipLaunchKernelGGL(tsg::tsgemm_mx_kernel<true>, dim3(g.P), dim3(tsg::MxTraits::THREADS), 0,
+                               static_cast<hipStream_t>(stream), a);
+        else
+            hipLaunchKernelGGL(tsg::tsgemm_mx_kernel<false>, dim3(g.P), dim3(tsg::MxTraits::THREADS), 0,
+                               static_cast<hipStream_t>(stream), a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TSGEMM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -362,13 +377,45 @@ int tsgemm_run_traced(const tsgemm_plan* p, const void* A, const void* B, void* 
 
 int tsgemm_run_mx(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB, void* C,
                   void* stream) {
-    return run_mx_impl(p, A, SFA, B, SFB, C, stream, nullptr);
+    return run_mx_impl(p, A, SFA, B, SFB, C, stream, nullptr, false);
 }
 
 int tsgemm_run_mx_traced(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB,
                          void* C, void* stream, int32_t* trace) {
     if (!trace) return fail(TSGEMM_EINVAL, "trace is NULL");
-    return run_mx_impl(p, A, SFA, B, SFB, C, stream, trace);
+    return run_mx_impl(p, A, SFA, B, SFB, C, stream, trace, false);
+}
+
+int64_t tsgemm_mx_packed_scale_bytes(const tsgemm_plan* p, int operand) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (!is_mx(p)) return fail(TSGEMM_EINVAL, "not a TSGEMM_MXFP8 plan (dtype %d)", p->dtype);
+    if (operand != 0 && operand != 1) return fail(TSGEMM_EINVAL, "operand must be 0 (SFA) or 1 (SFB), got %d", operand);
+    return mx_packed_bytes(p, operand == 0 ? p->m_blocks : p->n_blocks);
+}
+
+int tsgemm_mx_pack_scales(const tsgemm_plan* p, int operand, const void* SF, void* SFP, void* stream) {
+    const int64_t bytes = tsgemm_mx_packed_scale_bytes(p, operand);
+    if (bytes < 0) return (int)bytes;
+    if (bytes == 0) return TSGEMM_OK;  // no rows or K == 0: nothing to pack
+    if (!SF || !SFP) return fail(TSGEMM_EINVAL, "SF or SFP is NULL");
+    if ((reinterpret_cast<uintptr_t>(SF) & 3u) || (reinterpret_cast<uintptr_t>(SFP) & 15u))
+        return fail(TSGEMM_EINVAL, "SF must be 4-byte and SFP 16-byte aligned");
+    const int64_t rows = operand == 0 ? p->M : p->N;
+    const int64_t blocks = operand == 0 ? p->m_blocks : p->n_blocks;
+    const int64_t dwords = bytes / 4;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(tsg::tsgemm_mx_pack_kernel, dim3((unsigned)((dwords + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(SF), static_cast<uint8_t*>(SFP),
+                       rows, (uint32_t)(p->K / 32), (uint32_t)blocks, mx_groups(p));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TSGEMM_EHIP, "pack kernel launch failed: %s", hipGetErrorString(e));
+    return TSGEMM_OK;
+}
+
+int tsgemm_run_mx_packed(const tsgemm_plan* p, const void* A, const void* SFAP, const void* B, const void* SFBP,
+                         void* C, void* stream) {
+    return run_mx_impl(p, A, SFAP, B, SFBP, C, stream, nullptr, true);
 }
 
 int64_t tsgemm_num_tiles(const tsgemm_plan* p) {

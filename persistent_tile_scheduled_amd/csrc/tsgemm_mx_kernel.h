@@ -46,15 +46,16 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 struct MxArgs {
     const uint8_t* A;    // [M][K] E4M3
-    const uint8_t* SFA;  // [M][K/32] E8M0
+    const uint8_t* SFA;  // [M][K/32] E8M0, or packed (see tsgemm_mx_pack_kernel)
     const uint8_t* B;    // [N][K] E4M3
-    const uint8_t* SFB;  // [N][K/32] E8M0
+    const uint8_t* SFB;  // [N][K/32] E8M0, or packed
     uint16_t* C;         // [M][N] bf16
     int32_t* trace;      // optional (worker, iter, m, n) per processed tile
     int64_t M, N, K;
     uint32_t m_blocks, n_blocks, k_blocks, group;
     uint32_t P, max_iters, num_xcd;
     uint32_t cluster, col_major;
+    uint32_t n_groups;   // scale groups per tile: ceil(k_blocks / SG)
 };
 
 // acc += src0 x src1 with per-row E8M0 scales (byte 0 of each scale
@@ -137,6 +138,10 @@ __device__ __forceinline__ uint32_t mx_col_of_row(uint32_t rho) {
 __device__ __forceinline__ uint32_t mx_swz_a(uint32_t m) { return (m & 7u) ^ ((m >> 3) & 1u); }
 __device__ __forceinline__ uint32_t mx_swz_b(uint32_t n) { return ((n & 3u) | ((n >> 1) & 4u)) ^ ((n >> 2) & 1u); }
 
+// PACKED: SFA and SFB come in the tile-blocked layout of tsgemm_mx_pack_kernel,
+// so a wave's share of a scale group is 64 * SC_ROW contiguous bytes (one or two
+// cache lines per 8 lanes) instead of 64 rows' worth of separate cache lines.
+template <bool PACKED>
 __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     using T = MxTraits;
     constexpr int F = T::F, NA = T::NA, NB = T::NB, ND = T::ND, NS = T::NS, NSC = T::NSC, L = T::L;
@@ -172,7 +177,8 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         // lane%LPR of the group's 4*SG bytes (same offsets for SFA and SFB)
 #pragma unroll
         for (int i = 0; i < NS; ++i)
-            voff[ND + i] = (wave * 64u + i * (64u / T::LPR) + lane / T::LPR) * KB + (lane % T::LPR) * 16u;
+            voff[ND + i] = (wave * 64u + i * (64u / T::LPR) + lane / T::LPR) * (PACKED ? (uint32_t)T::SC_ROW : KB) +
+                           (lane % T::LPR) * 16u;
     }
 
     // ---- per-lane LDS read offsets (bytes from the stage origin) ----
@@ -222,8 +228,19 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         const int64_t sb_left = (args.N - n0) * kbs - kb0, sb_cap = (int64_t)T::BN * kbs;
         rs_a = rsrc_words(args.A + (m0 * args.K + k0) * live, live ? (uint32_t)(a_left < a_cap ? a_left : a_cap) : 0u);
         rs_b = rsrc_words(args.B + (n0 * args.K + k0) * live, live ? (uint32_t)(b_left < b_cap ? b_left : b_cap) : 0u);
-        rs_sa = rsrc_words(args.SFA + (m0 * kbs + kb0) * live, live ? (uint32_t)(sa_left < sa_cap ? sa_left : sa_cap) : 0u);
-        rs_sb = rsrc_words(args.SFB + (n0 * kbs + kb0) * live, live ? (uint32_t)(sb_left < sb_cap ? sb_left : sb_cap) : 0u);
+        if constexpr (PACKED) {
+            // group g of row block i: 256 rows x SC_ROW bytes at (i * n_groups + g) * 256 * SC_ROW
+            constexpr int64_t kGroupBytes = (int64_t)T::BM * T::SC_ROW;
+            const int64_t g = ld_k / T::SG;
+            rs_sa = rsrc_words(args.SFA + ((int64_t)ld.m_idx * args.n_groups + g) * kGroupBytes * live,
+                               live ? (uint32_t)kGroupBytes : 0u);
+            rs_sb = rsrc_words(args.SFB + ((int64_t)ld.n_idx * args.n_groups + g) * kGroupBytes * live,
+                               live ? (uint32_t)kGroupBytes : 0u);
+            (void)sa_left; (void)sa_cap; (void)sb_left; (void)sb_cap;
+        } else {
+            rs_sa = rsrc_words(args.SFA + (m0 * kbs + kb0) * live, live ? (uint32_t)(sa_left < sa_cap ? sa_left : sa_cap) : 0u);
+            rs_sb = rsrc_words(args.SFB + (n0 * kbs + kb0) * live, live ? (uint32_t)(sb_left < sb_cap ? sb_left : sb_cap) : 0u);
+        }
         if (live && ++ld_k == k_blocks) {
             ld_k = 0;
             ld.next_tile();
@@ -426,6 +443,28 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         epilogue();
     }
     wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
+}
+
+// Scale packing for the PACKED kernel: SF[rows][K/32] (row-major E8M0) ->
+// SFP[block][group][256][SC_ROW], block = 256-row block, group = SG consecutive
+// 128-deep slabs (SC_ROW = 4 * SG bytes of one row).  Rows past `rows` and
+// bytes past K/32 are written as 0.  One thread per output dword.
+__global__ void tsgemm_mx_pack_kernel(const uint8_t* SF, uint8_t* SFP, int64_t rows, uint32_t kb_bytes,
+                                      uint32_t blocks, uint32_t n_groups) {
+    constexpr uint32_t DW = MxTraits::SC_ROW / 4;  // dwords per row and group
+    const uint64_t total = (uint64_t)blocks * n_groups * MxTraits::BM * DW;
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const uint32_t d = (uint32_t)(t % DW);
+    const uint64_t rg = t / DW;                    // ((block * n_groups + group) * 256 + r)
+    const uint32_t r = (uint32_t)(rg % MxTraits::BM);
+    const uint64_t bg = rg / MxTraits::BM;
+    const uint32_t g = (uint32_t)(bg % n_groups), blk = (uint32_t)(bg / n_groups);
+    const int64_t row = (int64_t)blk * MxTraits::BM + r;
+    const uint32_t col = g * (uint32_t)MxTraits::SC_ROW + d * 4u;   // byte within the row, multiple of 4
+    uint32_t v = 0;
+    if (row < rows && col < kb_bytes) v = *(const uint32_t*)(SF + row * kb_bytes + col);  // kb_bytes % 4 == 0
+    *(uint32_t*)(SFP + t * 4) = v;
 }
 
 }  // namespace tsg

@@ -74,6 +74,14 @@ def test_mx_plan_info_and_dtype_mismatch():
     assert lib.tsgemm_run_mx_traced(p._h, None, None, None, None, None, None, None) == tsg.EINVAL
     assert "trace" in tsg.last_error()
     assert p.trace_rows() == 6 * 2
+    # packed scale arrays: blocks x ceil(k_blocks / 4) groups x 256 rows x 16 bytes
+    assert p.mx_packed_scale_bytes(0) == 4 * 1 * 4096 and p.mx_packed_scale_bytes(1) == 3 * 1 * 4096
+    big = tsg.Plan(8192, 8192, 8192, "mxfp8", 256, 256, 128, 8, 2)
+    assert big.mx_packed_scale_bytes(0) == 32 * 16 * 4096 == 8192 * 8192 // 32
+    assert lib.tsgemm_mx_packed_scale_bytes(p._h, 2) == tsg.EINVAL
+    assert lib.tsgemm_mx_packed_scale_bytes(q._h, 0) == tsg.EINVAL
+    assert lib.tsgemm_mx_pack_scales(p._h, 0, None, None, None) == tsg.EINVAL
+    assert lib.tsgemm_run_mx_packed(q._h, None, None, None, None, None, None) == tsg.EINVAL
 
 
 def test_null_plan_calls_fail_cleanly():

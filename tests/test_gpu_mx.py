@@ -138,6 +138,49 @@ def test_mx_trace_matches_oracle_schedule():
                      f"traced cm={cm} cs={cs}")
 
 
+# ---------------------------------------------------------------- packed scales
+def _pack_reference(SF, rows, K):
+    """The packed layout of tsgemm_mx_pack_scales written out directly:
+    [256-row block][group of 16 scale bytes][256 rows][16], zeros past the data."""
+    kb = K // 32
+    blocks, groups = -(-rows // 256), -(-(K // 128) // 4)
+    out = np.zeros((blocks, groups, 256, 16), np.uint8)
+    for b in range(blocks):
+        for g in range(groups):
+            r0, r1 = b * 256, min(rows, b * 256 + 256)
+            c0, c1 = g * 16, min(kb, g * 16 + 16)
+            out[b, g, : r1 - r0, : c1 - c0] = SF[r0:r1, c0:c1]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [(300, 264, 384), (520, 776, 1152), (256, 256, 512)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mx_packed_scales_layout_and_bit_identical_result(shape):
+    """tsgemm_mx_pack_scales writes exactly the documented permutation, and
+    tsgemm_run_mx_packed on it returns C bit for bit equal to tsgemm_run_mx
+    (same products, same order), within the bound of the oracle."""
+    M, N, K = shape
+    print(f"[case] mx packed {shape}", flush=True)
+    A, SFA, B, SFB = make_mx_inputs(M, N, K, seed=K + 1, spread=3)
+    plan = _plan(M, N, K, P=5, gs=2)
+    dev = [torch.from_numpy(x).to(DEV) for x in (A, SFA, B, SFB)]
+    packed = []
+    for op, (sf, rows) in enumerate(((dev[1], M), (dev[3], N))):
+        sfp = torch.full((plan.mx_packed_scale_bytes(op),), 0xAB, dtype=torch.uint8, device=DEV)
+        plan.mx_pack_scales(sf, sfp, op)
+        torch.cuda.synchronize()
+        assert np.array_equal(sfp.cpu().numpy(), _pack_reference((SFA, SFB)[op], rows, K)), f"operand {op}"
+        packed.append(sfp)
+    C1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    C2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    plan.run_mx(*dev, C1)
+    plan.run_mx_packed(dev[0], packed[0], dev[2], packed[1], C2)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    _check_bound(C2.cpu().double().numpy(), oracle.mx_gemm_f64(A, SFA, B, SFB), _mag(A, SFA, B, SFB),
+                 f"packed {shape}")
+
+
 # ---------------------------------------------------------------- edge cases
 def test_mx_empty_and_zero_k():
     z = torch.zeros(0, dtype=torch.uint8, device=DEV)
@@ -174,16 +217,30 @@ def test_mx_nan_codes_propagate():
 
 
 # ---------------------------------------------------------------- full size, sampled
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("name", list(MX_WORKLOADS))
-def test_mx_full_size_sampled(name):
+def test_mx_full_size_sampled(name, packed):
     """The benchmarked shape in the launch configuration the benchmark times
-    (one workgroup per CU, XCD remap on): every element written and finite,
-    4096 sampled outputs (including all four corners of the matrix) within the
-    bound, computed one by one by the oracle."""
+    (one workgroup per CU, XCD remap on; scales row-major or packed on the
+    device first): every element written and finite, 4096 sampled outputs
+    (including all four corners of the matrix) within the bound, computed one
+    by one by the oracle."""
     w = MX_WORKLOADS[name]
-    print(f"[case] mx full size {name}", flush=True)
+    print(f"[case] mx full size {name} packed={packed}", flush=True)
     A, SFA, B, SFB = mx_workload_inputs(w)
-    got = _run(_plan(w.M, w.N, w.K, P=w.num_workgroups, gs=w.group_size), A, SFA, B, SFB, guard=256)
+    plan = _plan(w.M, w.N, w.K, P=w.num_workgroups, gs=w.group_size)
+    if packed:
+        dev = [torch.from_numpy(x).to(DEV) for x in (A, SFA, B, SFB)]
+        sfp = [torch.empty((plan.mx_packed_scale_bytes(op),), dtype=torch.uint8, device=DEV) for op in (0, 1)]
+        plan.mx_pack_scales(dev[1], sfp[0], 0)
+        plan.mx_pack_scales(dev[3], sfp[1], 1)
+        buf = torch.full((w.M * w.N + 256,), float("nan"), dtype=torch.bfloat16, device=DEV)
+        plan.run_mx_packed(dev[0], sfp[0], dev[2], sfp[1], buf[: w.M * w.N].view(w.M, w.N))
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[w.M * w.N:].float()).all(), "write past the end of C"
+        got = buf[: w.M * w.N].view(w.M, w.N).cpu().double().numpy()
+    else:
+        got = _run(plan, A, SFA, B, SFB, guard=256)
     assert np.all(np.isfinite(got)), "non-finite output (unwritten tile?)"
     rng = np.random.default_rng(1)
     rows = np.concatenate([[0, 0, w.M - 1, w.M - 1], rng.integers(0, w.M, 4092)])
