@@ -78,8 +78,8 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsr
 #ifndef TSG_MX_SG
 #define TSG_MX_SG 4
 #endif
-#ifndef TSG_MX_SCALES_LAST
-#define TSG_MX_SCALES_LAST 1
+#ifndef TSG_MX_DMA_FIRST
+#define TSG_MX_DMA_FIRST 8
 #endif
 struct MxTraits {
     static constexpr int BM = 256, BN = 256, BK = 128, L = 2;
@@ -101,6 +101,9 @@ struct MxTraits {
     static constexpr int LPR = SG / 4;            // 16-byte DMA lanes per row and group
     static constexpr int NS = LPR;                // scale DMAs per wave and operand and group (64 rows)
     static constexpr int NSC = 2 * NS;
+    // data DMAs of a slab issued in the LAST k-step of the slab two back (with
+    // the scale DMAs); the remaining ND - DF go out during the next k-step
+    static constexpr int DF = (TSG_MX_DMA_FIRST > 0 && TSG_MX_DMA_FIRST < ND) ? TSG_MX_DMA_FIRST : ND;
     static_assert(SG == 4 || SG == 8, "scale group");
     static_assert(L == 2, "the slabs' DMA counts vary (scale groups): every wait is for all of them");
     static_assert(LDS <= 160 * 1024, "LDS");
@@ -247,12 +250,12 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         }
         ++ld_phase;
     };
-    // DMA q of a slab: A and B chunks, then (only when the slab starts a
-    // scale group) the group's scale DMAs, SFA then SFB -- with TSG_MX_SCALES_LAST
-    // 0 the scale DMAs come first instead.
+    // DMA q of a slab in issue order: A and B chunks [0, DF), then (only when
+    // the slab starts a scale group) the group's scale DMAs, SFA then SFB, then
+    // chunks [DF, ND).
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int qq = decltype(q_c)::value;
-        constexpr int q = TSG_MX_SCALES_LAST ? (qq < ND ? qq + NSC : qq - ND) : qq;
+        constexpr int q = qq < T::DF ? qq + NSC : (qq < T::DF + NSC ? qq - T::DF : qq);
         if constexpr (q < NSC) {
             constexpr int i = q % NS;
             if (sc_issue)
@@ -335,7 +338,8 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         constexpr int S0 = LAST ? kMxS0 : 0;
         constexpr int START = S0 > kMxGap ? S0 : kMxGap;
         constexpr int AVAIL = NSTEP - START - 1;
-        constexpr int D = LAST ? NSC + ND : 0;
+        constexpr int D = LAST ? T::DF + NSC : ND - T::DF;   // DMA ops [D0, D0 + D) of the issue order
+        constexpr int D0 = LAST ? 0 : T::DF + NSC;
         constexpr int DPER = D ? (D + AVAIL - 1) / AVAIL : 0;
         constexpr int PER = (R + AVAIL - 1) / AVAIL;
         static_assert(AVAIL * PER >= R && (D == 0 || AVAIL * DPER >= D), "k-step too short for its memory operations");
@@ -356,7 +360,9 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
                 if constexpr (D) {
                     constexpr int d0 = i * DPER;
                     constexpr int d1 = d0 + DPER < D ? d0 + DPER : D;
-                    static_for<d0, d1>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+                    static_for<d0, d1>([&](auto q_c) __attribute__((always_inline)) {
+                        dma_op(std::integral_constant<int, D0 + decltype(q_c)::value>{});
+                    });
                 }
                 constexpr int q0 = i * PER;
                 constexpr int q1 = q0 + PER < R ? q0 + PER : R;
@@ -417,7 +423,10 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
     for (int s = 0; s < L; ++s) {
         next_slab();
-        static_for<0, NSC + ND>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+        if (s + 1 < L)
+            static_for<0, NSC + ND>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+        else  // the last prologue slab's chunks [DF, ND) follow in the first k-step
+            static_for<0, T::DF + NSC>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
     }
     wait_vm<0>();
     lds_barrier();
