@@ -195,6 +195,8 @@ def main():
                     help="rewrite a 512 MiB scratch buffer before every timed launch (caches cold); "
                          "the per-launch events still bracket only the GEMM")
     ap.add_argument("--no-torch-context", action="store_true")
+    ap.add_argument("--epilogue", type=int, choices=[0, 64], default=0,
+                    help="fp16/bf16 epilogue: 0 = direct stores, 64 = C staged through LDS in 64-column chunks")
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="MX workload: pack the scales on the device each step (default) or feed them row-major")
     args = ap.parse_args()
@@ -226,7 +228,7 @@ def main():
         Ad, Bd = A.to(dev), B.to(dev)
         C = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=dev)
     plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
-                    w.num_stages, num_workgroups=w.num_workgroups)
+                    w.num_stages, num_workgroups=w.num_workgroups, store_block_N=0 if mx else args.epilogue)
     info = plan.info()
     P = plan.num_workgroups
     stream = torch.cuda.current_stream(dev)
@@ -296,6 +298,7 @@ def main():
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
             "tile": [w.block_M, w.block_N, w.block_K], "group_size": w.group_size,
             "num_stages": w.num_stages, "lds_slots": info["lds_slots"], "num_workgroups": P,
+            "store_block_N": info["store_block_N"],
             "inputs": (f"normal(0,1) MX-encoded (E4M3 + E8M0 per 32 along K), seed {w.seed}" if mx
                        else f"{w.dist}, seed {w.seed}"),
             **({"scales": ("row-major, packed on the device inside every step" if packed else "row-major")}

@@ -63,7 +63,7 @@ typedef struct tsgemm_info {
     int32_t lds_slots;       /* K-slabs resident in LDS: min(num_stages, LDS / stage) */
     int32_t stage_bytes;     /* (block_M*block_K + block_K*block_N) * 2; MXFP8:
                                 (block_M + block_N) * (block_K + 4)               */
-    int32_t lds_bytes;       /* lds_slots * stage_bytes                              */
+    int32_t lds_bytes;       /* lds_slots * stage_bytes (+ block_M * 128 with the chunked epilogue) */
     int64_t m_blocks, n_blocks, k_blocks, num_tiles;
     int32_t num_workgroups;  /* P; 0 while unresolved (default P before a device is seen) */
     int32_t waves;           /* waves of the busiest workgroup, ceil(ceil(m_blocks/cs) * n_blocks
@@ -72,6 +72,7 @@ typedef struct tsgemm_info {
     int32_t xcd_remap;       /* 1: workgroup -> worker id permuted so XCDs get compact tile blocks */
     int32_t cluster_size;    /* tile scheduler: workgroups per cluster (1 = none)     */
     int32_t column_major;    /* tile scheduler: 1 = transposed tile walk              */
+    int32_t store_block_N;   /* epilogue: 0 = direct stores, 64 = staged through LDS  */
 } tsgemm_info;
 
 /*
@@ -114,6 +115,17 @@ int tsgemm_set_waves(tsgemm_plan* plan, int waves);
  *     fastest, instead of column groups with n fastest (the transpose).
  * Results of tsgemm_run do not depend on either option. */
 int tsgemm_set_schedule(tsgemm_plan* plan, int column_major, int cluster_size);
+
+/* Epilogue (page "[Feature] Introduce tile scheduler #2441", diff of the
+ * persistent example: use_tma_store / store_block_N, the cast tile written to
+ * shared memory and stored in column blocks).  store_block_N = 0 (default):
+ * each lane stores its 16-byte pieces of C straight from registers; 64: the
+ * tile leaves in 64-column chunks staged through an LDS buffer of block_M x 64
+ * elements after the ring, every C row written as whole 128-byte segments.
+ * The ring gives up a slot where both do not fit (tsgemm_info.lds_slots).
+ * 4-wave kernels only (EUNSUPPORTED with 8 waves or MXFP8).  C is bit for bit
+ * the same either way. */
+int tsgemm_set_epilogue(tsgemm_plan* plan, int store_block_N);
 
 /* Enable (1, default) or disable (0) the XCD-aware workgroup -> worker id
  * permutation.  The schedule is defined on worker ids either way. */

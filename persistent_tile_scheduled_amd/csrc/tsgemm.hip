@@ -36,22 +36,26 @@ int fail(int code, const char* fmt, ...) {
 
 typedef void (*launch_fn)(const tsg::GemmArgs&, unsigned grid, hipStream_t);
 
-template <int DT, int BM, int BN, int BK, int L, int WGN>
+template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI>
 void launch(const tsg::GemmArgs& a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((tsg::tsgemm_kernel<DT, BM, BN, BK, L, WGN>), dim3(grid), dim3(64 * 2 * WGN), 0, s, a);
+    hipLaunchKernelGGL((tsg::tsgemm_kernel<DT, BM, BN, BK, L, WGN, EPI>), dim3(grid), dim3(64 * 2 * WGN), 0, s, a);
 }
 
 struct KernelEntry {
-    int dt, bm, bn, bk, slots, waves;
+    int dt, bm, bn, bk, slots, waves, epi;
     launch_fn fn;
 };
 
-#define TSG_SLOTS(DT, BM, BN, BK, WGN)                                                                     \
-    {DT, BM, BN, BK, 2, 2 * WGN, launch<DT, BM, BN, BK, 2, WGN>},                                          \
-    {DT, BM, BN, BK, 3, 2 * WGN, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 3 <= kLdsBytes) ? 3 : 2, WGN>}, \
-    {DT, BM, BN, BK, 4, 2 * WGN, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 4 <= kLdsBytes) ? 4 : 2, WGN>}, \
-    {DT, BM, BN, BK, 5, 2 * WGN, launch<DT, BM, BN, BK, ((BM * BK + BK * BN) * 2 * 5 <= kLdsBytes) ? 5 : 2, WGN>}
-#define TSG_TILE(DT, BM, BN, BK) TSG_SLOTS(DT, BM, BN, BK, 2), TSG_SLOTS(DT, BM, BN, BK, 4)
+// LDS of `S` ring slots plus the chunked epilogue's buffer fits?  Entries whose
+// slot count does not fit are compiled with 2 slots and never selected.
+#define TSG_FIT(BM, BN, BK, S, EPI) (((BM * BK + BK * BN) * 2 * S + BM * EPI * 2) <= kLdsBytes)
+#define TSG_SLOTS(DT, BM, BN, BK, WGN, EPI)                                                                 \
+    {DT, BM, BN, BK, 2, 2 * WGN, EPI, launch<DT, BM, BN, BK, 2, WGN, EPI>},                                 \
+    {DT, BM, BN, BK, 3, 2 * WGN, EPI, launch<DT, BM, BN, BK, TSG_FIT(BM, BN, BK, 3, EPI) ? 3 : 2, WGN, EPI>}, \
+    {DT, BM, BN, BK, 4, 2 * WGN, EPI, launch<DT, BM, BN, BK, TSG_FIT(BM, BN, BK, 4, EPI) ? 4 : 2, WGN, EPI>}, \
+    {DT, BM, BN, BK, 5, 2 * WGN, EPI, launch<DT, BM, BN, BK, TSG_FIT(BM, BN, BK, 5, EPI) ? 5 : 2, WGN, EPI>}
+#define TSG_TILE(DT, BM, BN, BK) \
+    TSG_SLOTS(DT, BM, BN, BK, 2, 0), TSG_SLOTS(DT, BM, BN, BK, 4, 0), TSG_SLOTS(DT, BM, BN, BK, 2, 64)
 
 const KernelEntry kKernels[] = {
     TSG_TILE(1, 128, 128, 32), TSG_TILE(1, 128, 128, 64), TSG_TILE(1, 256, 256, 32), TSG_TILE(1, 256, 256, 64),
@@ -64,17 +68,19 @@ int default_waves(int bm, int bn, int bk) {
     return 4;
 }
 
-const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots, int waves) {
+const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots, int waves, int epi) {
     for (const KernelEntry& e : kKernels)
-        if (e.dt == dt && e.bm == bm && e.bn == bn && e.bk == bk && e.slots == slots && e.waves == waves) return &e;
+        if (e.dt == dt && e.bm == bm && e.bn == bn && e.bk == bk && e.slots == slots && e.waves == waves &&
+            e.epi == epi)
+            return &e;
     return nullptr;
 }
 
-// LDS ring depth in block_K slabs: min(num_stages, LDS / stage, kMaxSlots);
-// 0 when two stages do not fit.
-int ring_slots(int bm, int bn, int bk, int stages) {
+// LDS ring depth in block_K slabs: min(num_stages, (LDS - epilogue buffer) /
+// stage, kMaxSlots); 0 when two stages do not fit.
+int ring_slots(int bm, int bn, int bk, int stages, int epi = 0) {
     const int stage = (bm * bk + bk * bn) * 2;
-    int slots = kLdsBytes / stage;
+    int slots = (kLdsBytes - bm * epi * 2) / stage;
     if (slots > stages) slots = stages;
     if (slots > kMaxSlots) slots = kMaxSlots;
     return slots >= 2 ? slots : 0;
@@ -115,6 +121,7 @@ struct tsgemm_plan {
     int xcd_remap; // 1 = permute workgroups so each XCD runs consecutive worker ids
     int cluster;   // workgroups per cluster (tile scheduler option), >= 1
     int col_major; // 1 = transposed tile walk (tile scheduler option)
+    int epi;       // 0 = direct stores, 64 = C staged through LDS in 64-column chunks
     const KernelEntry* kernel;  // fp16/bf16 kernel; NULL for an MXFP8 plan
 };
 
@@ -315,7 +322,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     if (mb * nb >= lim) { fail(TSGEMM_EUNSUPPORTED, "tile count must be below 2^31"); return nullptr; }
     const KernelEntry* k = dtype == TSGEMM_MXFP8
                                ? nullptr
-                               : find_kernel(dtype, block_M, block_N, block_K, slots, default_waves(block_M, block_N, block_K));
+                               : find_kernel(dtype, block_M, block_N, block_K, slots, default_waves(block_M, block_N, block_K), 0);
     if (!k && dtype != TSGEMM_MXFP8) { fail(TSGEMM_EUNSUPPORTED, "no kernel for this configuration"); return nullptr; }
     tsgemm_plan* p = new (std::nothrow) tsgemm_plan;
     if (!p) { fail(TSGEMM_ENOMEM, "out of host memory"); return nullptr; }
@@ -323,7 +330,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     p->dtype = dtype; p->bm = block_M; p->bn = block_N; p->bk = block_K;
     p->group = group_size; p->stages = num_stages; p->slots = slots;
     p->m_blocks = mb; p->n_blocks = nb; p->k_blocks = K / block_K; p->tiles = mb * nb;
-    p->P = 0; p->xcd_remap = 1; p->cluster = 1; p->col_major = 0; p->kernel = k;
+    p->P = 0; p->xcd_remap = 1; p->cluster = 1; p->col_major = 0; p->epi = 0; p->kernel = k;
     return p;
 }
 
@@ -341,9 +348,27 @@ int tsgemm_set_waves(tsgemm_plan* p, int waves) {
     if (waves == 0) waves = default_waves(p->bm, p->bn, p->bk);
     if (waves != 4 && waves != 8) return fail(TSGEMM_EINVAL, "waves must be 0, 4 or 8, got %d", waves);
     if (is_mx(p)) return waves == 4 ? TSGEMM_OK : fail(TSGEMM_EUNSUPPORTED, "the MXFP8 kernel runs 4 waves");
-    const KernelEntry* k = find_kernel(p->dtype, p->bm, p->bn, p->bk, p->slots, waves);
-    if (!k) return fail(TSGEMM_EUNSUPPORTED, "no %d-wave kernel for this configuration", waves);
+    const KernelEntry* k = find_kernel(p->dtype, p->bm, p->bn, p->bk, p->slots, waves, p->epi);
+    if (!k) return fail(TSGEMM_EUNSUPPORTED, "no %d-wave kernel for this configuration%s", waves,
+                        p->epi ? " with the chunked epilogue" : "");
     p->kernel = k;
+    return TSGEMM_OK;
+}
+
+int tsgemm_set_epilogue(tsgemm_plan* p, int store_block_N) {
+    g_err[0] = '\0';
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (store_block_N != 0 && store_block_N != 64)
+        return fail(TSGEMM_EINVAL, "store_block_N must be 0 (direct stores) or 64, got %d", store_block_N);
+    if (is_mx(p))
+        return store_block_N ? fail(TSGEMM_EUNSUPPORTED, "the MXFP8 kernel stores directly") : TSGEMM_OK;
+    const int slots = ring_slots(p->bm, p->bn, p->bk, p->stages, store_block_N);
+    if (slots < 2) return fail(TSGEMM_EUNSUPPORTED, "two stages and the epilogue buffer do not fit in LDS");
+    const KernelEntry* k = find_kernel(p->dtype, p->bm, p->bn, p->bk, slots, p->kernel->waves, store_block_N);
+    if (!k) return fail(TSGEMM_EUNSUPPORTED, "no %d-wave kernel with store_block_N %d", p->kernel->waves, store_block_N);
+    p->kernel = k;
+    p->slots = slots;
+    p->epi = store_block_N;
     return TSGEMM_OK;
 }
 
@@ -444,7 +469,7 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
     info->num_stages = p->stages;
     info->lds_slots = p->slots;
     info->stage_bytes = stage_bytes_of(p->dtype, p->bm, p->bn, p->bk);
-    info->lds_bytes = info->stage_bytes * p->slots;
+    info->lds_bytes = info->stage_bytes * p->slots + (p->epi ? p->bm * p->epi * 2 : 0);
     info->m_blocks = p->m_blocks; info->n_blocks = p->n_blocks;
     info->k_blocks = p->k_blocks; info->num_tiles = p->tiles;
     info->num_workgroups = p->P;  // explicit P only; default resolves at run time
@@ -453,6 +478,7 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
     info->xcd_remap = p->xcd_remap;
     info->cluster_size = p->cluster;
     info->column_major = p->col_major;
+    info->store_block_N = p->epi;
     return TSGEMM_OK;
 }
 

@@ -40,7 +40,7 @@ namespace tsg {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int DT, int BM, int BN, int BK, int L, int WGN>
+template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI = 0>
 struct GemmTraits {
     static constexpr int NW = 2 * WGN;                      // waves: 2 along M x WGN along N
     static constexpr int THREADS = 64 * NW;
@@ -52,7 +52,11 @@ struct GemmTraits {
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = STAGE * L;
+    // EPI = 64: the epilogue stages C through an LDS buffer of BM rows x 64
+    // columns after the ring (EPI = 0: direct stores from registers)
+    static constexpr int CHUNK_OFF = STAGE * L;
+    static constexpr int CHUNK_BYTES = EPI ? BM * EPI * 2 : 0;
+    static constexpr int LDS = STAGE * L + CHUNK_BYTES;
     static constexpr int NA = A_BYTES / (1024 * NW);        // DMA instructions per wave, A
     static constexpr int NB = B_BYTES / (1024 * NW);        // DMA instructions per wave, B
     static constexpr int NL = NA + NB;
@@ -65,13 +69,14 @@ struct GemmTraits {
                   "slab must split into whole 1 KiB DMAs per wave");
     static_assert(WGN == 2 || WGN == 4, "wave grid");
     static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(EPI == 0 || (EPI == 64 && WGN == 2 && WN % 64 == 0), "chunked epilogue: 64 columns, 4 waves");
     static_assert(CB >= 16, "B swizzle needs 16 chunks per row");
 };
 
 
-template <int DT, int BM, int BN, int BK, int L, int WGN>
+template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI = 0>
 __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) {
-    using T = GemmTraits<DT, BM, BN, BK, L, WGN>;
+    using T = GemmTraits<DT, BM, BN, BK, L, WGN, EPI>;
     constexpr int FM = T::FM, FN = T::FN, KS = T::KS, NA = T::NA, NB = T::NB, NL = T::NL;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
     const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem);
@@ -293,6 +298,67 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     const bool swap = (lg & 1u) != 0;  // odd lane groups hold the upper four columns of block 2t
     const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
     const uint32_t lane_off = (row0 * N + col0) * 2u;
+
+    // Chunked epilogue (the page's store_block_N path: the cast tile goes to
+    // shared memory and leaves in 64-column blocks), EPI = 64.  For chunk c
+    // (tile columns 64c .. 64c+63) the two waves holding those columns write
+    // their 16-byte pieces (row r, chunk-local 16-byte slot j at r*128 +
+    // (j ^ (r mod 8))*16, the same swizzle as the A rows); after a barrier all
+    // threads copy whole 128-byte rows out with 16-byte stores (8 threads per
+    // row, 32 rows per 256 threads and round); a second barrier frees the
+    // buffer for the next chunk.  The rounding is the direct path's, so C is
+    // bit-identical.
+    auto chunked_store = [&](__amdgpu_buffer_rsrc_t rc, uint32_t rows_left, uint32_t cols_left)
+                             __attribute__((always_inline)) {
+        if constexpr (EPI) {
+            constexpr int CH = BN / EPI;          // chunks per tile
+            constexpr int WPC = T::WN / EPI;      // chunks per wave column
+            constexpr int ROUNDS = BM * 8 / T::THREADS;
+            typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+            const uint32_t chunk = lds_base + T::CHUNK_OFF;
+            static_for<0, CH>([&](auto c_c) __attribute__((always_inline)) {
+                constexpr int c = decltype(c_c)::value;
+                if (wc == (uint32_t)(c / WPC)) {
+                    static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) {
+                        constexpr int fm = decltype(fm_c)::value;
+                        const uint32_t r = row0 + fm * 16;
+                        static_for<0, 2>([&](auto tt_c) __attribute__((always_inline)) {
+                            constexpr int tt = decltype(tt_c)::value;
+                            constexpr int t = (c % WPC) * 2 + tt;
+                            const f32x4 x = acc[fm][2 * t], y = acc[fm][2 * t + 1];
+                            const uint32_t x0 = cvt_pk<DT>(x[0], x[1]), x1 = cvt_pk<DT>(x[2], x[3]);
+                            const uint32_t y0 = cvt_pk<DT>(y[0], y[1]), y1 = cvt_pk<DT>(y[2], y[3]);
+                            const u32x4 v = swap ? u32x4{y0, y1, x0, x1} : u32x4{x0, x1, y0, y1};
+                            const uint32_t slot = (4u * tt + lg) ^ (r & 7u);
+                            *(lds_u32x4*)((__attribute__((address_space(3))) uint8_t*)(uintptr_t)(chunk + r * 128u + slot * 16u)) = v;
+                        });
+                    });
+                }
+                lds_barrier();  // the chunk is complete in LDS
+                static_for<0, ROUNDS>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    const uint32_t idx = i * T::THREADS + threadIdx.x;
+                    const uint32_t r = idx >> 3, j = idx & 7u;
+                    const u32x4 v = *(const lds_u32x4*)((__attribute__((address_space(3))) uint8_t*)(uintptr_t)(
+                        chunk + r * 128u + ((j ^ (r & 7u)) * 16u)));
+                    const uint32_t col = (uint32_t)c * EPI + 8u * j;
+                    const bool ok = r < rows_left && col < cols_left;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? (r * N + col) * 2u : 0x80000000u, 0, 0);
+                    store_gap();
+                });
+                lds_barrier();  // every read of the chunk done before it is rewritten
+            });
+            // the k == 0 clear, once for the whole tile: clearing inside the
+            // owner-only branches would make every accumulator a merge of two
+            // values and spill
+            static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) {
+                static_for<0, FN>([&](auto fn_c) __attribute__((always_inline)) {
+                    acc[decltype(fm_c)::value][decltype(fn_c)::value] = f32x4{0.f, 0.f, 0.f, 0.f};
+                });
+            });
+        }
+    };
+
     auto epilogue = [&]() __attribute__((always_inline)) {
         gap_nops();  // the tile's last MFMAs have written their accumulators
         const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
@@ -306,6 +372,9 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         const uint32_t cols_left = (uint32_t)((args.N - n0) < BN ? (args.N - n0) : BN);
         const uint32_t c_bytes = ((rows_left - 1u) * N + cols_left) * 2u;
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(args.C + (m0 * args.N + n0), c_bytes);
+        if constexpr (EPI) {
+            chunked_store(rc, rows_left, cols_left);
+        } else {
         static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) {
             constexpr int fm = decltype(fm_c)::value;
             const bool row_ok = row0 + fm * 16 < rows_left;
@@ -327,6 +396,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
+        }
     };
 
     // prologue: slabs 0..L-1 in flight (the last one's DMAs [DF, NL) follow in

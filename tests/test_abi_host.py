@@ -84,6 +84,27 @@ def test_mx_plan_info_and_dtype_mismatch():
     assert lib.tsgemm_run_mx_packed(q._h, None, None, None, None, None, None) == tsg.EINVAL
 
 
+def test_set_epilogue_validation_and_info():
+    lib = tsg.load()
+    p = tsg.Plan(1024, 1024, 1024, "bf16", 256, 256, 64, 4, 3)
+    assert p.info()["store_block_N"] == 0 and p.info()["lds_bytes"] == 2 * 65536
+    assert lib.tsgemm_set_epilogue(p._h, 32) == tsg.EINVAL
+    assert lib.tsgemm_set_epilogue(p._h, 64) == tsg.OK
+    inf = p.info()
+    assert (inf["store_block_N"], inf["lds_slots"], inf["lds_bytes"]) == (64, 2, 2 * 65536 + 256 * 128)
+    assert lib.tsgemm_set_waves(p._h, 8) == tsg.EUNSUPPORTED          # chunked epilogue: 4 waves only
+    assert lib.tsgemm_set_epilogue(p._h, 0) == tsg.OK and p.info()["store_block_N"] == 0
+    q = tsg.Plan(1024, 1024, 1024, "fp16", 128, 128, 64, 4, 5)
+    assert q.info()["lds_slots"] == 5
+    assert lib.tsgemm_set_epilogue(q._h, 64) == tsg.OK
+    assert (q.info()["lds_slots"], q.info()["lds_bytes"]) == (4, 4 * 32768 + 128 * 128)   # ring gives up a slot
+    w8 = tsg.Plan(1024, 1024, 1024, "bf16", 256, 256, 64, 4, 3, waves=8)
+    assert lib.tsgemm_set_epilogue(w8._h, 64) == tsg.EUNSUPPORTED
+    mx = tsg.Plan(1024, 1024, 1024, "mxfp8", 256, 256, 128, 4, 2)
+    assert lib.tsgemm_set_epilogue(mx._h, 64) == tsg.EUNSUPPORTED
+    assert lib.tsgemm_set_epilogue(mx._h, 0) == tsg.OK
+
+
 def test_null_plan_calls_fail_cleanly():
     lib = tsg.load()
     assert lib.tsgemm_num_tiles(None) == tsg.EINVAL

@@ -302,3 +302,47 @@ def test_schedule_options_parity_256(cm, cs, waves):
     assert torch.isnan(guard.float()).all()
     ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), oracle.BF16)
     _check_close(C.double().numpy(), _bits_to_f64(ref_bits, "bf16"), "options 256")
+
+
+# ---------------------------------------------------------------- chunked epilogue
+EPI_TILES = [(128, 128, 32, 5), (128, 128, 64, 5), (256, 256, 32, 4), (256, 256, 64, 3)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("tile", EPI_TILES, ids=lambda t: "x".join(map(str, t)))
+def test_chunked_epilogue_bit_identical(dtype, tile):
+    """store_block_N = 64 (C staged through LDS in 64-column chunks) gives C
+    bit for bit equal to the direct stores, on ragged shapes with several
+    tiles per worker, and within tolerance of the oracle."""
+    bm, bn, bk, S = tile
+    M, N, K = 3 * bm - 40, 2 * bn + 24, 5 * bk
+    print(f"[case] chunked epilogue {dtype} {tile}", flush=True)
+    dist = "uniform" if dtype == "fp16" else "normal_sqrtk"   # the workloads' distributions per dtype
+    A, B = make_inputs(M, N, K, dtype, dist, seed=bm + bk)
+    direct = tsg.Plan(M, N, K, dtype, bm, bn, bk, 2, S, num_workgroups=4)
+    chunked = tsg.Plan(M, N, K, dtype, bm, bn, bk, 2, S, num_workgroups=4, store_block_N=64)
+    assert chunked.info()["store_block_N"] == 64
+    C1, g1 = _run(direct, A, B, dtype, guard=64)
+    C2, g2 = _run(chunked, A, B, dtype, guard=64)
+    assert torch.isnan(g2.float()).all(), "write past the end of C"
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[dtype])
+    _check_close(C2.double().numpy(), _bits_to_f64(ref_bits, dtype), f"chunked {tile}")
+
+
+def test_chunked_epilogue_full_size_bit_identical():
+    """8192^3 bf16 in the benchmarked configuration: chunked and direct
+    epilogues write identical C."""
+    w = WORKLOADS["cfg3_8192_bf16"]
+    print("[case] chunked epilogue 8192^3", flush=True)
+    A, B = workload_inputs(w)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    outs = []
+    for sbn in (0, 64):
+        plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size, w.num_stages,
+                        store_block_N=sbn)
+        C = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        plan.run(Ad, Bd, C)
+        torch.cuda.synchronize()
+        outs.append(C)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
