@@ -29,7 +29,7 @@ enum { DT_FP16 = 1, DT_BF16 = 2 };
 #endif
 constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA issues
 #ifndef TSG_DMA_FIRST
-#define TSG_DMA_FIRST 12  // DMAs per slab issued in its first k-step of issue (0: all)
+#define TSG_DMA_FIRST 14  // DMAs per slab issued in its first k-step of issue (0: all)
 #endif
 #ifndef TSG_GAP
 #define TSG_GAP 4
@@ -138,6 +138,26 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rs
     // s_nop: one wait state between the M0 write the compiler emits and its use
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                  : "memory");
+}
+
+// Descriptor words from a byte address held in scalar registers.
+__device__ __forceinline__ i32x4 rsrc_words_u64(uint64_t a, uint32_t bytes) {
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));  // stride 0
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = (int)kRawBufferFlags;
+    return r;
+}
+
+// The same DMA with its LDS target base + OFF written to M0 inside the asm:
+// the add sits next to its DMA (one scalar instruction, no copy of the base)
+// and the compiler knows M0 is overwritten.
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16_at(uint32_t lds_base_addr, uint32_t voff, i32x4 rsrc) {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(lds_base_addr), "i"(OFF)
+                 : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {

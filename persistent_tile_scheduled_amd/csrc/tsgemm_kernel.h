@@ -143,39 +143,80 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     }
 
     // ---- loader: its own scheduler copy, L slabs ahead of the MMA ----
+    // Per tile the loader forms the byte address of its first A slab (row
+    // block m, column 0) and B slab (row 0, column block n) and the ranges the
+    // descriptors may span; per slab it only steps them (A by BK columns, B by
+    // BK rows).  The scalar work that sits between two MFMAs is then a few
+    // adds and selects instead of 64-bit products and compares: the wave
+    // that issues them is the one that issues the MFMAs.
+    //   A: range = rows * K * 2 - k0 * 2 bytes from the slab origin, rows =
+    //      min(M - m0, BM): rows past M read zeros, and the range never runs
+    //      past row m0 + rows - 1 of A;
+    //   B: every slab but the tile's last spans BK full rows; the last slab's
+    //      range stops at the end of B (columns past N in its last row read
+    //      zeros; elsewhere they read finite neighbours that are never stored).
+    // BM*K*2 and BK*N*2 are below 2^31 (checked when the plan is created).
     TileScheduler ld;
     ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     ld.init(wid);
-    uint32_t ld_k = 0, ld_phase = 0;
+    uint32_t ld_k = 0, ld_slot = 0;
+    uint64_t a_ptr = 0, b_ptr = 0;
+    uint32_t a_num = 0, a_dec = 0, b_cap = 0, b_last = 0;
+    const uint32_t M32 = (uint32_t)args.M;
+    const uint64_t b_step = (uint64_t)BK * N * 2u;
     i32x4 rs_a, rs_b;
-    uint32_t dma_lds = 0;
+    uint32_t dma_lds = 0, ld_lds = lds_base + wave * NA * 1024u;
 
-    // descriptors and LDS target for the loader's next slab, then advance it;
-    // past the end the descriptors have zero range (the DMA writes zeros
-    // into a stage nobody reads) so every slab issues the same instructions
-    auto next_slab = [&]() __attribute__((always_inline)) {
-        dma_lds = lds_base + (ld_phase % L) * T::STAGE + wave * NA * 1024u;
-        const bool live = k_blocks != 0 && ld.valid();
-        const int64_t m0 = live ? (int64_t)ld.m_idx * BM : 0, n0 = live ? (int64_t)ld.n_idx * BN : 0;
-        const int64_t k0 = (int64_t)ld_k * BK;
-        const int64_t a_left = ((args.M - m0) * args.K - k0) * 2, a_cap = (int64_t)BM * args.K * 2;
-        const int64_t b_left = ((args.K - k0) * args.N - n0) * 2, b_cap = (int64_t)BK * args.N * 2;
-        const uint32_t a_bytes = live ? (uint32_t)(a_left < a_cap ? a_left : a_cap) : 0u;
-        const uint32_t b_bytes = live ? (uint32_t)(b_left < b_cap ? b_left : b_cap) : 0u;
-        rs_a = rsrc_words(args.A + (m0 * args.K + k0) * live, a_bytes);
-        rs_b = rsrc_words(args.B + (k0 * args.N + n0) * live, b_bytes);
-        if (live && ++ld_k == k_blocks) {
+    // ranges for the loader's current tile; zero past the end of the schedule
+    // (the DMAs then write zeros into a stage nobody reads, so every slab
+    // issues the same instructions)
+    auto tile_ranges = [&]() __attribute__((always_inline)) {
+        const bool live = ld.valid();
+        const uint32_t m0 = ld.m_idx * BM, n0 = ld.n_idx * BN;
+        const uint32_t rows = live ? (M32 - m0 < (uint32_t)BM ? M32 - m0 : (uint32_t)BM) : 0u;
+        a_ptr = reinterpret_cast<uint64_t>(args.A) + (live ? (uint64_t)m0 * K * 2u : 0u);
+        b_ptr = reinterpret_cast<uint64_t>(args.B) + (live ? (uint64_t)n0 * 2u : 0u);
+        a_num = rows * K * 2u;
+        a_dec = live ? BK * 2u : 0u;
+        b_cap = live ? (uint32_t)BK * N * 2u : 0u;
+        b_last = live ? ((uint32_t)BK * N - n0) * 2u : 0u;
+    };
+    // descriptors and LDS target of the loader's next slab
+    auto slab_desc = [&]() __attribute__((always_inline)) {
+        dma_lds = ld_lds;
+        rs_a = rsrc_words_u64(a_ptr, a_num);
+        rs_b = rsrc_words_u64(b_ptr, ld_k + 1u == k_blocks ? b_last : b_cap);
+    };
+    // step the loader to the slab after
+    auto slab_advance = [&]() __attribute__((always_inline)) {
+        a_ptr += BK * 2u;
+        a_num -= a_dec;
+        b_ptr += b_step;
+        if (++ld_slot == (uint32_t)L) {
+            ld_slot = 0;
+            ld_lds -= (L - 1) * T::STAGE;
+        } else {
+            ld_lds += T::STAGE;
+        }
+        if (++ld_k == k_blocks) {
             ld_k = 0;
             ld.next_tile();
+            tile_ranges();
         }
-        ++ld_phase;
     };
+    auto next_slab = [&]() __attribute__((always_inline)) {
+        slab_desc();
+        slab_advance();
+    };
+    tile_ranges();
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int q = decltype(q_c)::value;
+        // the LDS target is formed inside the DMA's own asm, next to it, not
+        // hoisted with the others into one gap between two MFMAs
         if constexpr (q < NA)
-            dma16(dma_lds + q * 1024u, voff[q], rs_a);
+            dma16_at<q * 1024u>(dma_lds, voff[q], rs_a);
         else
-            dma16(dma_lds + T::A_BYTES - wave * NA * 1024u + (wave * NB + (q - NA)) * 1024u, voff[q], rs_b);
+            dma16_at<(uint32_t)T::A_BYTES + (q - NA) * 1024u>(dma_lds + wave * (NB - NA) * 1024u, voff[q], rs_b);
     };
 
     // ---- fragments: two register sets for A and B, the one the MFMAs of this
@@ -223,6 +264,16 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         set_addr(ks_c, st);
         static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, r_c); });
     };
+    // The address a read op needs, formed one MFMA ahead of the read (an add
+    // right before its read would stall the read on the add): read op 0 forms
+    // ra, the first half of each B pair forms rb[fn]; the others reuse them.
+    auto prep_op = [&](auto ks_c, auto r_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int KSN = decltype(ks_c)::value, r = decltype(r_c)::value;
+        if constexpr (r == 0)
+            ra = lds_base + st + a_off[KSN];
+        else if constexpr (r <= 2 * FN && (r - 1) % 2 == 0)
+            rb[(r - 1) / 2] = lds_base + st + b_off[(r - 1) / 2] + KSN * 32 * (BN * 2);
+    };
 
     // One 32-deep k-step: FM*FN MFMAs (fm-major) from register set CUR,
     // accumulating into tiles that the epilogue left at zero (the k == 0
@@ -240,7 +291,6 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr bool SAME = decltype(same_c)::value;
         constexpr int NXT = SAME ? CUR : 1 - CUR;
         constexpr bool LAST = decltype(last_c)::value;
-        if constexpr (LAST) next_slab();  // scalar only; the DMA itself waits for the barrier
         constexpr int NSTEP = FM * FN;
         constexpr int S0 = LAST ? 2 : 0;                   // MFMAs issued before the barrier
         constexpr int START = S0 > kGap ? S0 : kGap;       // first step with memory operations
@@ -255,16 +305,32 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
         constexpr int QR = SAME ? 0 : R;                   // reads, spread evenly
         constexpr int PER = QR ? (QR + AVAIL - 1) / AVAIL : 0;
-        if constexpr (!LAST) set_addr(ksn_c, read_st);
+        // LAST: the next slab's descriptors after the first MFMA (scalar only;
+        // the DMAs themselves wait for the barrier), the loader's step late in
+        // the k-step where no memory operation is issued
+        // (any step after the first works: the DMAs of this slab use the
+        // descriptors formed at step 0)
+        constexpr int MEM_END = START + (D ? (D - 1) * DS + 1 : 0) > START + (PER ? (QR + PER - 1) / PER : 0)
+                                    ? START + (D ? (D - 1) * DS + 1 : 0) : START + (PER ? (QR + PER - 1) / PER : 0);
+        constexpr int ADV = MEM_END < NSTEP - 1 ? MEM_END : NSTEP - 1;
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / FN, fn = s % FN;
             const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
             mfma16x16x32<DT>(acc[fm][fn], bv, fa[CUR][fm]);
+            if constexpr (LAST && s == 0) slab_desc();
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
-                set_addr(ksn_c, read_st);
+            }
+            if constexpr (LAST && s == ADV) slab_advance();
+            if constexpr (s + 1 >= START) {
+                // addresses of the reads issued in the next step
+                constexpr int p0 = (s + 1 - START) * PER;
+                constexpr int p1 = p0 + PER < QR ? p0 + PER : QR;
+                static_for<p0, (p1 > p0 ? p1 : p0)>([&](auto q_c) __attribute__((always_inline)) {
+                    prep_op(ksn_c, q_c, read_st);
+                });
             }
             if constexpr (s >= START) {
                 constexpr int i = s - START;
@@ -279,6 +345,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         });
         if constexpr (SAME) {
             gap_nops();
+            set_addr(ksn_c, read_st);
             static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(cur_c, r_c); });
         }
     };
