@@ -204,52 +204,107 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     const uint32_t sa_off = a_row * T::SC_ROW + h, sb_off = T::SC_B + b_row * T::SC_ROW + h;
 
     // ---- loader: its own scheduler copy, L slabs ahead of the math ----
+    // Per tile the loader forms the byte addresses of its first slab of A, B
+    // (row blocks m and n, column 0) and of their scales, and the ranges the
+    // descriptors may span; per slab it only steps them (A and B by BK bytes,
+    // row-major scales by BK/32 bytes, packed scales by one group record per
+    // group).  The scalar work between two MFMAs is then a few adds and
+    // selects: the wave that issues it also issues the MFMAs.
+    //   A: range = rows * K - k0 bytes from the slab origin, rows =
+    //      min(M - m0, BM): rows past M read zeros and the range never runs
+    //      past row m0 + rows - 1 (B likewise with the columns of C);
+    //   row-major scales: rows * K/32 - k0/32 bytes (scale bytes of slabs past
+    //      K in a partial last group are never read);
+    //   packed scales: one 256-row group record.
+    // BM*K is below 2^31 (checked when the plan is created).
     TileScheduler ld;
     ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     ld.init(wid);
-    uint32_t ld_k = 0, ld_phase = 0, ld_grp = 0;
+    constexpr uint32_t kGroupBytes = (uint32_t)T::BM * T::SC_ROW;
+    const uint32_t M32 = (uint32_t)args.M;
+    uint32_t ld_k = 0, ld_slot = 0, ld_grp = 0;
+    uint64_t a_ptr = 0, b_ptr = 0, sa_ptr = 0, sb_ptr = 0;
+    uint32_t a_num = 0, b_num = 0, sa_num = 0, sb_num = 0, dec = 0, sdec = 0;
+    bool ld_live = false;
     i32x4 rs_a, rs_b, rs_sa, rs_sb;
-    uint32_t dma_lds = 0, sc_lds = 0;
+    uint32_t dma_lds = 0, sc_lds = 0, ld_lds = lds_base;
     bool sc_issue = false;
 
-    // Descriptors and LDS targets of the loader's next slab, then advance it.
-    // Past the end the descriptors have zero range: the DMA then writes zeros
-    // into a stage nobody reads, so every slab issues the same data DMAs.  A
-    // slab that starts a scale group (k % SG == 0) also fetches the group's
-    // scales into ring entry (group count) % 2.
-    auto next_slab = [&]() __attribute__((always_inline)) {
-        dma_lds = lds_base + (ld_phase % L) * T::STAGE;
-        const bool live = k_blocks != 0 && ld.valid();
-        sc_issue = live && (ld_k % T::SG) == 0;
-        sc_lds = lds_base + T::SC_OFF + (ld_grp & 1u) * T::SC_ENTRY + wave * 64u * T::SC_ROW;
-        ld_grp += sc_issue ? 1u : 0u;
-        const int64_t m0 = live ? (int64_t)ld.m_idx * T::BM : 0, n0 = live ? (int64_t)ld.n_idx * T::BN : 0;
-        const int64_t k0 = (int64_t)ld_k * T::BK, kb0 = k0 / 32, kbs = args.K / 32;
-        const int64_t a_left = (args.M - m0) * args.K - k0, a_cap = (int64_t)T::BM * args.K;
-        const int64_t b_left = (args.N - n0) * args.K - k0, b_cap = (int64_t)T::BN * args.K;
-        const int64_t sa_left = (args.M - m0) * kbs - kb0, sa_cap = (int64_t)T::BM * kbs;
-        const int64_t sb_left = (args.N - n0) * kbs - kb0, sb_cap = (int64_t)T::BN * kbs;
-        rs_a = rsrc_words(args.A + (m0 * args.K + k0) * live, live ? (uint32_t)(a_left < a_cap ? a_left : a_cap) : 0u);
-        rs_b = rsrc_words(args.B + (n0 * args.K + k0) * live, live ? (uint32_t)(b_left < b_cap ? b_left : b_cap) : 0u);
+    // ranges for the loader's current tile; zero past the end of the schedule
+    // (the data DMAs then write zeros into a stage nobody reads, so every slab
+    // issues the same data DMAs)
+    auto tile_ranges = [&]() __attribute__((always_inline)) {
+        const bool live = ld.valid();
+        ld_live = live;
+        const uint32_t m0 = ld.m_idx * T::BM, n0 = ld.n_idx * T::BN;
+        const uint32_t rows = live ? (M32 - m0 < (uint32_t)T::BM ? M32 - m0 : (uint32_t)T::BM) : 0u;
+        const uint32_t cols = live ? (N - n0 < (uint32_t)T::BN ? N - n0 : (uint32_t)T::BN) : 0u;
+        a_ptr = reinterpret_cast<uint64_t>(args.A) + (live ? (uint64_t)m0 * K : 0u);
+        b_ptr = reinterpret_cast<uint64_t>(args.B) + (live ? (uint64_t)n0 * K : 0u);
+        a_num = rows * K;
+        b_num = cols * K;
+        dec = live ? (uint32_t)T::BK : 0u;
         if constexpr (PACKED) {
             // group g of row block i: 256 rows x SC_ROW bytes at (i * n_groups + g) * 256 * SC_ROW
-            constexpr int64_t kGroupBytes = (int64_t)T::BM * T::SC_ROW;
-            const int64_t g = ld_k / T::SG;
-            rs_sa = rsrc_words(args.SFA + ((int64_t)ld.m_idx * args.n_groups + g) * kGroupBytes * live,
-                               live ? (uint32_t)kGroupBytes : 0u);
-            rs_sb = rsrc_words(args.SFB + ((int64_t)ld.n_idx * args.n_groups + g) * kGroupBytes * live,
-                               live ? (uint32_t)kGroupBytes : 0u);
-            (void)sa_left; (void)sa_cap; (void)sb_left; (void)sb_cap;
+            sa_ptr = reinterpret_cast<uint64_t>(args.SFA) + (live ? (uint64_t)ld.m_idx * args.n_groups * kGroupBytes : 0u);
+            sb_ptr = reinterpret_cast<uint64_t>(args.SFB) + (live ? (uint64_t)ld.n_idx * args.n_groups * kGroupBytes : 0u);
+            sa_num = live ? kGroupBytes : 0u;
+            sb_num = sa_num;
         } else {
-            rs_sa = rsrc_words(args.SFA + (m0 * kbs + kb0) * live, live ? (uint32_t)(sa_left < sa_cap ? sa_left : sa_cap) : 0u);
-            rs_sb = rsrc_words(args.SFB + (n0 * kbs + kb0) * live, live ? (uint32_t)(sb_left < sb_cap ? sb_left : sb_cap) : 0u);
+            sa_ptr = reinterpret_cast<uint64_t>(args.SFA) + (live ? (uint64_t)m0 * KB : 0u);
+            sb_ptr = reinterpret_cast<uint64_t>(args.SFB) + (live ? (uint64_t)n0 * KB : 0u);
+            sa_num = rows * KB;
+            sb_num = cols * KB;
+            sdec = live ? (uint32_t)T::BK / 32u : 0u;
         }
-        if (live && ++ld_k == k_blocks) {
+    };
+    // descriptors and LDS targets of the loader's next slab.  A slab that
+    // starts a scale group (k % SG == 0) also fetches the group's scales into
+    // ring entry (group count) % 2.
+    auto slab_desc = [&]() __attribute__((always_inline)) {
+        dma_lds = ld_lds;
+        sc_issue = ld_live && (ld_k % T::SG) == 0;
+        sc_lds = lds_base + T::SC_OFF + (ld_grp & 1u) * T::SC_ENTRY + wave * 64u * T::SC_ROW;
+        rs_a = rsrc_words_u64(a_ptr, a_num);
+        rs_b = rsrc_words_u64(b_ptr, b_num);
+        rs_sa = rsrc_words_u64(sa_ptr, sa_num);
+        rs_sb = rsrc_words_u64(sb_ptr, sb_num);
+    };
+    // step the loader to the slab after
+    auto slab_advance = [&]() __attribute__((always_inline)) {
+        ld_grp += sc_issue ? 1u : 0u;
+        a_ptr += (uint32_t)T::BK;
+        a_num -= dec;
+        b_ptr += (uint32_t)T::BK;
+        b_num -= dec;
+        if constexpr (PACKED) {
+            if (sc_issue) {
+                sa_ptr += kGroupBytes;
+                sb_ptr += kGroupBytes;
+            }
+        } else {
+            sa_ptr += (uint32_t)T::BK / 32u;
+            sa_num -= sdec;
+            sb_ptr += (uint32_t)T::BK / 32u;
+            sb_num -= sdec;
+        }
+        if (++ld_slot == (uint32_t)L) {
+            ld_slot = 0;
+            ld_lds -= (L - 1) * T::STAGE;
+        } else {
+            ld_lds += T::STAGE;
+        }
+        if (++ld_k == k_blocks) {
             ld_k = 0;
             ld.next_tile();
+            tile_ranges();
         }
-        ++ld_phase;
     };
+    auto next_slab = [&]() __attribute__((always_inline)) {
+        slab_desc();
+        slab_advance();
+    };
+    tile_ranges();
     // DMA q of a slab in issue order: A and B chunks [0, DF), then (only when
     // the slab starts a scale group) the group's scale DMAs, SFA then SFB, then
     // chunks [DF, ND).
@@ -261,9 +316,10 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
             if (sc_issue)
                 dma16(sc_lds + (q < NS ? 0u : (uint32_t)T::SC_B) + i * 1024u, voff[ND + i], q < NS ? rs_sa : rs_sb);
         } else if constexpr (q - NSC < NA) {
-            dma16(dma_lds + (wave * NA + (q - NSC)) * 1024u, voff[q - NSC], rs_a);
+            // the LDS target is formed inside the DMA's own asm, next to it
+            dma16_at<(q - NSC) * 1024u>(dma_lds + wave * NA * 1024u, voff[q - NSC], rs_a);
         } else {
-            dma16(dma_lds + T::A_BYTES + (wave * NB + (q - NSC - NA)) * 1024u, voff[q - NSC], rs_b);
+            dma16_at<(uint32_t)T::A_BYTES + (q - NSC - NA) * 1024u>(dma_lds + wave * NB * 1024u, voff[q - NSC], rs_b);
         }
     };
 
@@ -333,7 +389,6 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int NXT = 1 - CUR;
         constexpr bool LAST = decltype(last_c)::value;
-        if constexpr (LAST) next_slab();
         constexpr int NSTEP = F * F;
         constexpr int S0 = LAST ? kMxS0 : 0;
         constexpr int START = S0 > kMxGap ? S0 : kMxGap;
@@ -343,6 +398,12 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         constexpr int DPER = D ? (D + AVAIL - 1) / AVAIL : 0;
         constexpr int PER = (R + AVAIL - 1) / AVAIL;
         static_assert(AVAIL * PER >= R && (D == 0 || AVAIL * DPER >= D), "k-step too short for its memory operations");
+        // LAST: the next slab's descriptors after the first MFMA (scalar only;
+        // the DMAs themselves wait for the barrier), the loader's step after
+        // the k-step's last DMA (any later step works: the DMAs of this slab
+        // use the descriptors formed at step 0)
+        constexpr int ADV = START + (D ? (D + DPER - 1) / DPER : 0) < NSTEP - 1 ? START + (D ? (D + DPER - 1) / DPER : 0)
+                                                                              : NSTEP - 1;
         if constexpr (!LAST) set_addr(ksn_c, read_st, read_scb);
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
@@ -350,6 +411,8 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
             const i32x8 b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7));
             const i32x8 a8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fa[CUR][fm][0], fa[CUR][fm][1], 0, 1, 2, 3, 4, 5, 6, 7));
             mfma_mx32(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
+            if constexpr (LAST && s == 0) slab_desc();
+            if constexpr (LAST && s == ADV) slab_advance();
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<0>();    // slab phase+1 (and its scale group) has landed
                 lds_barrier();   // ... for every wave; stage phase and scale entries read are free
