@@ -84,6 +84,20 @@ def test_ragged_shapes_every_kernel(dtype, tile, S, waves):
     _full_check(M, N, K, dtype, dist, 100 + S, bm, bn, bk, 2, S, P=3, waves=waves)
 
 
+@pytest.mark.parametrize("kb", [1, 2, 3])
+@pytest.mark.parametrize("tile", TILES)
+def test_short_k_many_tiles_per_worker(tile, kb):
+    """One to three K slabs per tile and several tiles per worker: the loader
+    sets up each tile's ranges every one to three slabs (last-slab range of B,
+    partial row and column tiles, slot wrap across tiles)."""
+    bm, bn, bk = tile
+    M, N, K = 3 * bm + 40, 2 * bn + 24, kb * bk
+    dtype = "fp16" if kb != 2 else "bf16"
+    dist = "uniform" if dtype == "fp16" else "normal_sqrtk"
+    print(f"[case] short K {dtype} {tile} k_blocks={kb} {M}x{N}x{K}", flush=True)
+    _full_check(M, N, K, dtype, dist, 700 + kb, bm, bn, bk, 2, 3, P=2)
+
+
 @pytest.mark.parametrize("P", [1, 2, 5, 8, 64, 300])
 def test_worker_counts(P):
     print(f"[case] P={P}", flush=True)
