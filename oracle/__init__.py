@@ -72,6 +72,8 @@ def _load():
     lib.oracle_round_array.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     u8 = ctypes.POINTER(ctypes.c_uint8)
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = ctypes.c_double
@@ -96,6 +98,11 @@ def _ptr(a: np.ndarray, ctype):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads used by later oracle calls (timing only; results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def gemm_f64(A, B) -> np.ndarray:

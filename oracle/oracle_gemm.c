@@ -130,3 +130,13 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of later oracle calls (n >= 1); timing only, the sums do not depend on it. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
