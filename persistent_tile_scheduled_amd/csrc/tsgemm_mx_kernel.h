@@ -79,7 +79,7 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsr
 #define TSG_MX_SG 4
 #endif
 #ifndef TSG_MX_DMA_FIRST
-#define TSG_MX_DMA_FIRST 8
+#define TSG_MX_DMA_FIRST 11  // data DMAs of a slab issued in its first k-step of issue (of 16)
 #endif
 struct MxTraits {
     static constexpr int BM = 256, BN = 256, BK = 128, L = 2;
