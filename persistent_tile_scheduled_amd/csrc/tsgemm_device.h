@@ -40,7 +40,6 @@ constexpr int kGap = TSG_GAP;  // MFMAs between the last read of a fragment set 
 // (MFMAs here are asm, so the compiler inserts no wait states for them).
 __device__ __forceinline__ void gap_nops() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 __device__ __forceinline__ void store_gap() { asm volatile("s_nop 7\n\ts_nop 7" ::: "memory"); }
-constexpr int kMaxThreads = 512;
 constexpr uint32_t kRawBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
 
 struct GemmArgs {
@@ -160,14 +159,4 @@ __device__ __forceinline__ void dma16_at(uint32_t lds_base_addr, uint32_t voff, 
                  : "memory", "m0", "scc");
 }
 
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    // all four words are wave-uniform; readfirstlane keeps them in SGPRs
-    i32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));  // stride 0
-    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-    r.w = (int)kRawBufferFlags;
-    return r;
-}
 }  // namespace tsg
