@@ -98,6 +98,50 @@ def test_short_k_many_tiles_per_worker(tile, kb):
     _full_check(M, N, K, dtype, dist, 700 + kb, bm, bn, bk, 2, 3, P=2)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_special_values_follow_ieee(dtype):
+    """NaN and infinite inputs and an overflowing sum.  IEEE arithmetic fixes
+    which outputs are NaN and which are +-Inf (the oracle sums in binary64,
+    the kernel in binary32, and no finite partial sum here comes near either
+    range), so the patterns must match exactly; every other output is held to
+    the usual tolerance.
+      row 3:     A[3, 10] = NaN                       -> NaN
+      column 7:  B[20, 7] = +Inf, A[5, 20] = 0        -> sign(A[i, 20]) * Inf, NaN at row 5
+      column 9:  B[30, 9] = -Inf, B[31, 9] = +Inf     -> NaN or +-Inf by the signs of A[i, 30:32]
+      (100, 100): A[100, 50] * B[50, 100] above the format's largest value -> +Inf"""
+    M, N, K = 256, 256, 128
+    # the bf16 workloads' distribution: with uniform[-1,1] inputs |C| reaches
+    # 4-8, where one bf16 ulp (2^-5) exceeds the elementwise bound
+    dist = "uniform" if dtype == "fp16" else "normal_sqrtk"
+    A, B = make_inputs(M, N, K, dtype, dist, 900 + len(dtype))
+    A, B = A.clone(), B.clone()
+    big = 60000.0 if dtype == "fp16" else 3.0e38
+    A[3, 10] = float("nan")
+    B[20, 7] = float("inf")
+    A[5, 20] = 0.0
+    B[30, 9] = float("-inf")
+    B[31, 9] = float("inf")
+    A[100, :] = 0.0
+    A[100, 50] = big
+    B[50, 100] = 2.0
+    print(f"[case] special values {dtype}", flush=True)
+    plan = tsg.Plan(M, N, K, dtype, 128, 128, 64, 2, 2, num_workgroups=3)
+    C, _ = _run(plan, A, B, dtype)
+    got = C.double().numpy()
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[dtype])
+    ref = _bits_to_f64(ref_bits, dtype)
+    assert np.isinf(ref[100, 100]) and ref[100, 100] > 0, "the overflow case must overflow in the oracle"
+    assert np.isnan(ref[3]).all() and np.isnan(ref[5, 7]) and np.isinf(ref[0, 7])
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), \
+        f"NaN pattern differs: kernel {np.isnan(got).sum()}, oracle {np.isnan(ref).sum()}"
+    inf = np.isinf(ref)
+    assert np.array_equal(np.isinf(got), inf), "Inf pattern differs"
+    assert np.array_equal(np.sign(got[inf]), np.sign(ref[inf])), "Inf signs differ"
+    fin = np.isfinite(ref)
+    err = np.abs(got[fin] - ref[fin])
+    assert np.all(err <= 2e-3 * (np.abs(ref[fin]) + 1.0)), f"max err {err.max()}"
+
+
 @pytest.mark.parametrize("P", [1, 2, 5, 8, 64, 300])
 def test_worker_counts(P):
     print(f"[case] P={P}", flush=True)
