@@ -159,4 +159,15 @@ __device__ __forceinline__ void dma16_at(uint32_t lds_base_addr, uint32_t voff, 
                  : "memory", "m0", "scc");
 }
 
+// The LDS-DMA in two pieces: M0 = base + OFF, and later the load that uses
+// it.  The caller keeps other M0 writers out from between them and leaves at
+// least one instruction between the two (the M0-to-LDS-DMA wait state).
+template <uint32_t OFF>
+__device__ __forceinline__ void set_m0(uint32_t lds_base_addr) {
+    asm volatile("s_add_u32 m0, %0, %1" ::"s"(lds_base_addr), "i"(OFF) : "m0", "scc");
+}
+__device__ __forceinline__ void dma16_m0(uint32_t voff, i32x4 rsrc) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc) : "memory");
+}
+
 }  // namespace tsg

@@ -209,14 +209,35 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         slab_advance();
     };
     tile_ranges();
+    // One DMA in one piece (prologue): its LDS target is written to M0 inside
+    // the DMA's own asm.
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int q = decltype(q_c)::value;
-        // the LDS target is formed inside the DMA's own asm, next to it, not
-        // hoisted with the others into one gap between two MFMAs
         if constexpr (q < NA)
             dma16_at<q * 1024u>(dma_lds, voff[q], rs_a);
         else
             dma16_at<(uint32_t)T::A_BYTES + (q - NA) * 1024u>(dma_lds + wave * (NB - NA) * 1024u, voff[q], rs_b);
+    };
+    // The same DMA in two pieces (main loop): M0 written in the MFMA gap
+    // before the one that issues the load, so neither gap carries the wait
+    // state an M0 write needs before its LDS-DMA.  Nothing else in the loop
+    // writes M0 (the fragment reads do not use it); a load is always issued
+    // before the next M0 write, in program order, with an MFMA between each
+    // M0 write and its load.
+    auto m0_op = [&](auto q_c) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        if constexpr (q < NA)
+            set_m0<q * 1024u>(dma_lds);
+        else
+            set_m0<(uint32_t)T::A_BYTES + (q - NA) * 1024u>(dma_lds + wave * (NB - NA) * 1024u);
+    };
+    auto load_op = [&](auto q_c) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        const uint32_t v = voff[q];
+        if constexpr (q < NA)
+            dma16_m0(v, rs_a);
+        else
+            dma16_m0(v, rs_b);
     };
 
     // ---- fragments: two register sets for A and B, the one the MFMAs of this
@@ -334,13 +355,16 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             }
             if constexpr (s >= START) {
                 constexpr int i = s - START;
-                if constexpr (D && i % DS == 0 && i / DS < D) dma_op(std::integral_constant<int, D0 + i / DS>{});
+                if constexpr (D && i % DS == 0 && i / DS < D) load_op(std::integral_constant<int, D0 + i / DS>{});
                 constexpr int q0 = i * PER;
                 constexpr int q1 = q0 + PER < QR ? q0 + PER : QR;
                 static_for<q0, q1>([&](auto q_c) __attribute__((always_inline)) {
                     read_op(std::integral_constant<int, NXT>{}, q_c);
                 });
             }
+            // M0 for the DMA issued in the next step, after this step's load
+            if constexpr (D && s + 1 >= START && (s + 1 - START) % DS == 0 && (s + 1 - START) / DS < D)
+                m0_op(std::integral_constant<int, D0 + (s + 1 - START) / DS>{});
             __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (SAME) {
