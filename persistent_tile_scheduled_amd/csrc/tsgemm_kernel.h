@@ -160,12 +160,23 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     ld.init(wid);
     uint32_t ld_k = 0, ld_slot = 0;
-    uint64_t a_ptr = 0, b_ptr = 0;
-    uint32_t a_num = 0, a_dec = 0, b_cap = 0, b_last = 0;
+    uint32_t a_dec = 0, b_cap = 0, b_last = 0;
     const uint32_t M32 = (uint32_t)args.M;
     const uint64_t b_step = (uint64_t)BK * N * 2u;
+    // The loader's state is the descriptors themselves (words 0-1: the
+    // slab origin, word 2: the range) and the LDS target of its next slab; the
+    // DMAs read them in place.
     i32x4 rs_a, rs_b;
-    uint32_t dma_lds = 0, ld_lds = lds_base + wave * NA * 1024u;
+    uint32_t dma_lds = lds_base + wave * NA * 1024u;
+    // With a slab's DMAs split over two k-steps, the loader steps in the
+    // first k-step of a slab (after the split slab's remaining DMAs), else in
+    // the slab's last k-step (after all of them).
+    constexpr bool kSplitAdvance = KS == 2 && T::DF < NL;
+    auto add64 = [](i32x4& r, uint64_t d) __attribute__((always_inline)) {
+        const uint64_t a = (((uint64_t)(uint32_t)r.y) << 32 | (uint32_t)r.x) + d;  // stride bits are 0
+        r.x = (int)(uint32_t)a;
+        r.y = (int)(uint32_t)(a >> 32);
+    };
 
     // ranges for the loader's current tile; zero past the end of the schedule
     // (the DMAs then write zeros into a stage nobody reads, so every slab
@@ -174,39 +185,32 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         const bool live = ld.valid();
         const uint32_t m0 = ld.m_idx * BM, n0 = ld.n_idx * BN;
         const uint32_t rows = live ? (M32 - m0 < (uint32_t)BM ? M32 - m0 : (uint32_t)BM) : 0u;
-        a_ptr = reinterpret_cast<uint64_t>(args.A) + (live ? (uint64_t)m0 * K * 2u : 0u);
-        b_ptr = reinterpret_cast<uint64_t>(args.B) + (live ? (uint64_t)n0 * 2u : 0u);
-        a_num = rows * K * 2u;
         a_dec = live ? BK * 2u : 0u;
         b_cap = live ? (uint32_t)BK * N * 2u : 0u;
         b_last = live ? ((uint32_t)BK * N - n0) * 2u : 0u;
+        rs_a = rsrc_words_u64(reinterpret_cast<uint64_t>(args.A) + (live ? (uint64_t)m0 * K * 2u : 0u), rows * K * 2u);
+        rs_b = rsrc_words_u64(reinterpret_cast<uint64_t>(args.B) + (live ? (uint64_t)n0 * 2u : 0u),
+                              k_blocks == 1u ? b_last : b_cap);
     };
-    // descriptors and LDS target of the loader's next slab
-    auto slab_desc = [&]() __attribute__((always_inline)) {
-        dma_lds = ld_lds;
-        rs_a = rsrc_words_u64(a_ptr, a_num);
-        rs_b = rsrc_words_u64(b_ptr, ld_k + 1u == k_blocks ? b_last : b_cap);
-    };
-    // step the loader to the slab after
+    // step the loader to the slab after, once every DMA of the current one
+    // has been issued
     auto slab_advance = [&]() __attribute__((always_inline)) {
-        a_ptr += BK * 2u;
-        a_num -= a_dec;
-        b_ptr += b_step;
+        add64(rs_a, BK * 2u);
+        rs_a.z -= (int)a_dec;
+        add64(rs_b, b_step);
         if (++ld_slot == (uint32_t)L) {
             ld_slot = 0;
-            ld_lds -= (L - 1) * T::STAGE;
+            dma_lds -= (L - 1) * T::STAGE;
         } else {
-            ld_lds += T::STAGE;
+            dma_lds += T::STAGE;
         }
         if (++ld_k == k_blocks) {
             ld_k = 0;
             ld.next_tile();
             tile_ranges();
+        } else {
+            rs_b.z = (int)(ld_k + 1u == k_blocks ? b_last : b_cap);
         }
-    };
-    auto next_slab = [&]() __attribute__((always_inline)) {
-        slab_desc();
-        slab_advance();
     };
     tile_ranges();
     // One DMA in one piece (prologue): its LDS target is written to M0 inside
@@ -317,6 +321,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int START = S0 > kGap ? S0 : kGap;       // first step with memory operations
         constexpr int AVAIL = NSTEP - START - 1;
         static_assert(AVAIL >= 2, "k-step too short for its memory operations");
+        static_assert(LAST ? T::DF <= AVAIL + 1 : NL - T::DF <= AVAIL + 1, "every DMA of a slab needs a gap");
         // LAST issues DMAs [0, DF) of slab phase+L; the following first k-step
         // of the next slab issues [DF, NL) of the same slab
         constexpr int D = LAST ? T::DF : (SAME ? 0 : NL - T::DF);
@@ -326,11 +331,9 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
         constexpr int QR = SAME ? 0 : R;                   // reads, spread evenly
         constexpr int PER = QR ? (QR + AVAIL - 1) / AVAIL : 0;
-        // LAST: the next slab's descriptors after the first MFMA (scalar only;
-        // the DMAs themselves wait for the barrier), the loader's step late in
-        // the k-step where no memory operation is issued
-        // (any step after the first works: the DMAs of this slab use the
-        // descriptors formed at step 0)
+        // The loader's step (in the k-step that issues the last DMAs of a
+        // slab) late in the k-step, after its last DMA, where no memory
+        // operation is issued: the DMAs read the descriptors in place.
         constexpr int MEM_END = START + (D ? (D - 1) * DS + 1 : 0) > START + (PER ? (QR + PER - 1) / PER : 0)
                                     ? START + (D ? (D - 1) * DS + 1 : 0) : START + (PER ? (QR + PER - 1) / PER : 0);
         constexpr int ADV = MEM_END < NSTEP - 1 ? MEM_END : NSTEP - 1;
@@ -339,12 +342,10 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             constexpr int fm = s / FN, fn = s % FN;
             const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
             mfma16x16x32<DT>(acc[fm][fn], bv, fa[CUR][fm]);
-            if constexpr (LAST && s == 0) slab_desc();
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
             }
-            if constexpr (LAST && s == ADV) slab_advance();
             if constexpr (s + 1 >= START) {
                 // addresses of the reads issued in the next step
                 constexpr int p0 = (s + 1 - START) * PER;
@@ -362,6 +363,9 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                     read_op(std::integral_constant<int, NXT>{}, q_c);
                 });
             }
+            // after this gap's DMA: with short k-steps the last DMA can sit in
+            // the gap ADV itself
+            if constexpr ((kSplitAdvance ? !LAST : LAST) && s == ADV) slab_advance();
             // M0 for the DMA issued in the next step, after this step's load
             if constexpr (D && s + 1 >= START && (s + 1 - START) % DS == 0 && (s + 1 - START) / DS < D)
                 m0_op(std::integral_constant<int, D0 + (s + 1 - START) / DS>{});
@@ -493,11 +497,13 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // prologue: slabs 0..L-1 in flight (the last one's DMAs [DF, NL) follow in
     // the first k-step), the first k-step's fragments read
     for (int s = 0; s < L; ++s) {
-        next_slab();
-        if (s + 1 < L)
+        if (s + 1 < L) {
             static_for<0, NL>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
-        else
+            slab_advance();
+        } else {
             static_for<0, T::DF>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+            if constexpr (!kSplitAdvance) slab_advance();
+        }
     }
     wait_vm<(L - 2) * NL + T::DF < 63 ? (L - 2) * NL + T::DF : 63>();
     lds_barrier();
