@@ -129,16 +129,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// One 16-byte-per-lane DMA from a buffer into LDS.  Issued as inline asm so
-// the compiler does not treat every later LDS read as dependent on it (it
-// cannot tell the stage being filled from the stage being read); the kernel
-// waits on vmcnt itself before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-    // s_nop: one wait state between the M0 write the compiler emits and its use
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-                 : "memory");
-}
-
 // Descriptor words from a byte address held in scalar registers.
 __device__ __forceinline__ i32x4 rsrc_words_u64(uint64_t a, uint32_t bytes) {
     i32x4 r;
@@ -149,9 +139,14 @@ __device__ __forceinline__ i32x4 rsrc_words_u64(uint64_t a, uint32_t bytes) {
     return r;
 }
 
-// The same DMA with its LDS target base + OFF written to M0 inside the asm:
-// the add sits next to its DMA (one scalar instruction, no copy of the base)
-// and the compiler knows M0 is overwritten.
+// One 16-byte-per-lane DMA from a buffer into LDS, its LDS target base + OFF
+// written to M0 inside the same asm (one scalar instruction next to the DMA;
+// s_nop: the wait state between an M0 write and the LDS-DMA that uses it).
+// Inline asm, so the compiler does not treat every later LDS read as
+// dependent on it (it cannot tell the stage being filled from the stage
+// being read); the kernel waits on vmcnt itself before the barrier that
+// publishes a stage.  Every M0 write in the kernels is inside these helpers:
+// no asm operand asks the compiler for a value in M0.
 template <uint32_t OFF>
 __device__ __forceinline__ void dma16_at(uint32_t lds_base_addr, uint32_t voff, i32x4 rsrc) {
     asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"

@@ -264,7 +264,9 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     auto slab_desc = [&]() __attribute__((always_inline)) {
         dma_lds = ld_lds;
         sc_issue = ld_live && (ld_k % T::SG) == 0;
-        sc_lds = lds_base + T::SC_OFF + (ld_grp & 1u) * T::SC_ENTRY + wave * 64u * T::SC_ROW;
+        // wave-uniform by construction; readfirstlane keeps it in an SGPR
+        // for the DMA's M0 add
+        sc_lds = __builtin_amdgcn_readfirstlane(lds_base + T::SC_OFF + (ld_grp & 1u) * T::SC_ENTRY + wave * 64u * T::SC_ROW);
         rs_a = rsrc_words_u64(a_ptr, a_num);
         rs_b = rsrc_words_u64(b_ptr, b_num);
         rs_sa = rsrc_words_u64(sa_ptr, sa_num);
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         if constexpr (q < NSC) {
             constexpr int i = q % NS;
             if (sc_issue)
-                dma16(sc_lds + (q < NS ? 0u : (uint32_t)T::SC_B) + i * 1024u, voff[ND + i], q < NS ? rs_sa : rs_sb);
+                dma16_at<(q < NS ? 0u : (uint32_t)T::SC_B) + i * 1024u>(sc_lds, voff[ND + i], q < NS ? rs_sa : rs_sb);
         } else if constexpr (q - NSC < NA) {
             // the LDS target is formed inside the DMA's own asm, next to it
             dma16_at<(q - NSC) * 1024u>(dma_lds + wave * NA * 1024u, voff[q - NSC], rs_a);
