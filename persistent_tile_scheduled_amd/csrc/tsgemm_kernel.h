@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // One 32-deep k-step: FM*FN MFMAs (fm-major) from register set CUR,
     // accumulating into tiles that the epilogue left at zero (the k == 0
     // clear), with the memory operations for what follows between them: the
-    // DMA (LAST only) and the reads of the next k-step into set NXT.  No read
+    // DMAs and the reads of the next k-step into set NXT.  No read
     // into a set starts within kGap MFMAs of the last MFMA that read it: an
     // MFMA may still be fetching its operands, and a second wave on the SIMD
     // can delay it.  LAST (the slab's last k-step) first waits for the next
@@ -331,9 +331,10 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
         constexpr int QR = SAME ? 0 : R;                   // reads, spread evenly
         constexpr int PER = QR ? (QR + AVAIL - 1) / AVAIL : 0;
-        // The loader's step (in the k-step that issues the last DMAs of a
-        // slab) late in the k-step, after its last DMA, where no memory
-        // operation is issued: the DMAs read the descriptors in place.
+        // The loader's step, in the k-step that issues a slab's last DMAs: in
+        // the first gap after all of this k-step's memory operations, or in
+        // the last gap after its DMA when the operations fill the k-step (the
+        // DMAs read the descriptors in place, so none may follow the step).
         constexpr int MEM_END = START + (D ? (D - 1) * DS + 1 : 0) > START + (PER ? (QR + PER - 1) / PER : 0)
                                     ? START + (D ? (D - 1) * DS + 1 : 0) : START + (PER ? (QR + PER - 1) / PER : 0);
         constexpr int ADV = MEM_END < NSTEP - 1 ? MEM_END : NSTEP - 1;
