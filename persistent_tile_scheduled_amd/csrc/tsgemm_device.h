@@ -31,6 +31,12 @@ constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA i
 #ifndef TSG_DMA_FIRST
 #define TSG_DMA_FIRST 14  // DMAs per slab issued in its first k-step of issue (0: all)
 #endif
+#ifndef TSG_EPI_INTERLEAVE
+#define TSG_EPI_INTERLEAVE 1  // 256x256 four-wave kernel: C stores between the MFMAs
+#endif
+#ifndef TSG_EPI_FIRST
+#define TSG_EPI_FIRST 4  // of its 8 row blocks per wave, those stored in the tile's last k-step
+#endif
 #ifndef TSG_GAP
 #define TSG_GAP 4
 #endif
@@ -65,6 +71,14 @@ __device__ __forceinline__ void mfma16x16x32(f32x4& acc, i16x8 a, i16x8 b) {
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
     else
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// The same MFMA with a zero accumulator input (the k == 0 clear): acc = a*b.
+template <int DT>
+__device__ __forceinline__ void mfma16x16x32_clear(f32x4& acc, i16x8 a, i16x8 b) {
+    if constexpr (DT == DT_FP16)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
 }
 
 // Two fp32 accumulators (held in AGPRs) -> one dword of two 16-bit values

@@ -300,6 +300,59 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             rb[(r - 1) / 2] = lds_base + st + b_off[(r - 1) / 2] + KSN * 32 * (BN * 2);
     };
 
+    // ---- the MMA's tile scheduler and each lane's place in C ----
+    TileScheduler sched;
+    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
+    const bool swap = (lg & 1u) != 0;  // odd lane groups hold the upper four columns of block 2t
+    const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
+    const uint32_t lane_off = (row0 * N + col0) * 2u;
+
+    // Interleaved epilogue (four waves, 256x256 tiles, two k-steps per slab,
+    // direct stores): a tile's C leaves between MFMAs instead of after them.
+    // Row block fm is final after MFMA fm*FN + FN-1 of the tile's last k-step.
+    // Blocks fm < kEpiFirst send each of their FN/2 stores kEpiLag + 2t MFMAs
+    // later in that k-step; the rest are final too late for it, and their
+    // stores go out in the next tile's first k-step, store t of block fm after
+    // MFMA (fm - kEpiFirst)*FN + 2t, before that k-step's first MFMA on block
+    // fm.  Half and half measured best: the last k-step already carries the
+    // slab barrier, most of the next slab's DMAs and its first reads.  A tile's first k-step uses the MFMA with a zero accumulator
+    // input (the k == 0 clear), so no accumulator is ever cleared by a
+    // register write.  The first tile's first k-step stores nothing (an empty
+    // store window); the last tile of a worker stores its second half after
+    // the loop.  Stores are two MFMAs apart, so a store's data registers stay
+    // intact for 32+ cycles before the next conversion (what store_gap gives
+    // the plain epilogue).
+    constexpr bool kEpiInterleave = TSG_EPI_INTERLEAVE && KS == 2 && EPI == 0 && WGN == 2 && FM == 8 && FN == 8;
+    constexpr int kEpiLag = 3;    // MFMAs between a block's last MFMA and its first conversion
+    constexpr int kEpiFirst = TSG_EPI_FIRST;  // row blocks stored in the tile's own last k-step
+    static_assert(!kEpiInterleave || (kEpiFirst - 1) * FN + FN - 1 + kEpiLag + 2 * (FN / 2 - 1) < FM * FN,
+                  "first-part stores must fit in the k-step");
+    __amdgpu_buffer_rsrc_t e_rc = make_rsrc(args.C, 0u);
+    uint32_t e_rows = 0, e_cols = 0;
+    // the store window of the MMA's current tile (and its trace row)
+    auto epi_state = [&]() __attribute__((always_inline)) {
+        const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
+        if (args.trace != nullptr && threadIdx.x == 0) {
+            int32_t* row = args.trace + 4 * ((size_t)wid * args.max_iters + sched.iter);
+            *(int4*)row = make_int4((int)wid, (int)sched.iter, (int)m_idx, (int)n_idx);
+            store_gap();
+        }
+        const int64_t m0 = (int64_t)m_idx * BM, n0 = (int64_t)n_idx * BN;
+        e_rows = (uint32_t)((args.M - m0) < BM ? (args.M - m0) : BM);
+        e_cols = (uint32_t)((args.N - n0) < BN ? (args.N - n0) : BN);
+        e_rc = make_rsrc(args.C + (m0 * args.N + n0), ((e_rows - 1u) * N + e_cols) * 2u);
+    };
+    // store t of row block fm (16 rows x 32 columns of the wave's sub-tile)
+    auto epi_op = [&](auto fm_c, auto t_c) __attribute__((always_inline)) {
+        constexpr int fm = decltype(fm_c)::value, t = decltype(t_c)::value;
+        const f32x4 x = acc[fm][2 * t], y = acc[fm][2 * t + 1];
+        const uint32_t x0 = cvt_pk<DT>(x[0], x[1]), x1 = cvt_pk<DT>(x[2], x[3]);
+        const uint32_t y0 = cvt_pk<DT>(y[0], y[1]), y1 = cvt_pk<DT>(y[2], y[3]);
+        const u32x4 v = swap ? u32x4{y0, y1, x0, x1} : u32x4{x0, x1, y0, y1};
+        const bool ok = row0 + fm * 16 < e_rows && col0 + 32u * t < e_cols;
+        __builtin_amdgcn_raw_buffer_store_b128(v, e_rc, (ok ? lane_off : 0x80000000u) + t * 64, fm * 16 * N * 2, 0);
+    };
+
     // One 32-deep k-step: FM*FN MFMAs (fm-major) from register set CUR,
     // accumulating into tiles that the epilogue left at zero (the k == 0
     // clear), with the memory operations for what follows between them: the
@@ -311,7 +364,11 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // phase+L into the stage just consumed and reads the next slab's first
     // k-step; otherwise it reads k-step KSN of the current stage.  SAME (an
     // odd tail slab) refills set CUR after its MFMAs.
-    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c) __attribute__((always_inline)) {
+    // EPH: 0 no stores, 1 the current tile's stores of blocks fm < kEpiFirst
+    // (its last k-step), 2 the previous tile's other stores (the tile's first
+    // k-step, whose MFMAs start from zero).
+    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c, auto eph_c) __attribute__((always_inline)) {
+        constexpr int EPH = decltype(eph_c)::value;
         constexpr int CUR = decltype(cur_c)::value;
         constexpr bool SAME = decltype(same_c)::value;
         constexpr int NXT = SAME ? CUR : 1 - CUR;
@@ -342,7 +399,10 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / FN, fn = s % FN;
             const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            mfma16x16x32<DT>(acc[fm][fn], bv, fa[CUR][fm]);
+            if constexpr (EPH == 2)
+                mfma16x16x32_clear<DT>(acc[fm][fn], bv, fa[CUR][fm]);
+            else
+                mfma16x16x32<DT>(acc[fm][fn], bv, fa[CUR][fm]);
             if constexpr (LAST && s == S0 - 1) {
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
@@ -367,6 +427,21 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             // after this gap's DMA: with short k-steps the last DMA can sit in
             // the gap ADV itself
             if constexpr ((kSplitAdvance ? !LAST : LAST) && s == ADV) slab_advance();
+            if constexpr (EPH == 1) {
+                static_for<0, kEpiFirst>([&](auto fm_c) __attribute__((always_inline)) {
+                    static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
+                        constexpr int fm = decltype(fm_c)::value, t = decltype(t_c)::value;
+                        if constexpr (s == fm * FN + FN - 1 + kEpiLag + 2 * t) epi_op(fm_c, t_c);
+                    });
+                });
+            } else if constexpr (EPH == 2) {
+                static_for<kEpiFirst, FM>([&](auto fm_c) __attribute__((always_inline)) {
+                    static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
+                        constexpr int fm = decltype(fm_c)::value, t = decltype(t_c)::value;
+                        if constexpr (s == (fm - kEpiFirst) * FN + 2 * t) epi_op(fm_c, t_c);
+                    });
+                });
+            }
             // M0 for the DMA issued in the next step, after this step's load
             if constexpr (D && s + 1 >= START && (s + 1 - START) % DS == 0 && (s + 1 - START) / DS < D)
                 m0_op(std::integral_constant<int, D0 + (s + 1 - START) / DS>{});
@@ -381,6 +456,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     using TRUE_ = std::integral_constant<bool, true>;
     using FALSE_ = std::integral_constant<bool, false>;
 
@@ -389,11 +465,6 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // asm so each stays next to its store instead of all being hoisted.  Lanes
     // outside C get a vector offset past the descriptor's range and are
     // dropped; the row block goes into the scalar offset.
-    TileScheduler sched;
-    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
-    const bool swap = (lg & 1u) != 0;  // odd lane groups hold the upper four columns of block 2t
-    const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
-    const uint32_t lane_off = (row0 * N + col0) * 2u;
 
     // Chunked epilogue (the page's store_block_N path: the cast tile goes to
     // shared memory and leaves in 64-column blocks), EPI = 64.  For chunk c
@@ -515,26 +586,54 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // alternate inside the slab.  One k-step per slab: slabs go in pairs; an
     // odd last slab refills set 0 after its MFMAs so every tile starts on set 0.
     uint32_t phase = 0;
+    bool pend = false;  // a tile's second-half stores are still to go out
     for (sched.init(wid); sched.valid(); sched.next_tile()) {
-        if constexpr (KS == 2) {
+        if constexpr (kEpiInterleave) {
+            // rotated: the tile's first k-step, then (last k-step of slab k,
+            // first k-step of slab k+1) pairs, then its last k-step; one code
+            // path per tile, so the accumulators stay put
+            kstep(I0{}, FALSE_{}, I1{}, (phase % L) * T::STAGE, FALSE_{}, I2{});
+            for (uint32_t k = 0; k + 1u < k_blocks; ++k, ++phase) {
+                kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{});
+                kstep(I0{}, FALSE_{}, I1{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{});
+            }
+            epi_state();  // after the previous tile's last stores
+            kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I1{});
+            ++phase;
+        } else if constexpr (KS == 2) {
             for (uint32_t k = 0; k < k_blocks; ++k, ++phase) {
                 const uint32_t st_cur = (phase % L) * T::STAGE;
                 const uint32_t st_next = ((phase + 1u) % L) * T::STAGE;
-                kstep(I0{}, FALSE_{}, I1{}, st_cur, FALSE_{});
-                kstep(I1{}, TRUE_{}, I0{}, st_next, FALSE_{});
+                kstep(I0{}, FALSE_{}, I1{}, st_cur, FALSE_{}, I0{});
+                kstep(I1{}, TRUE_{}, I0{}, st_next, FALSE_{}, I0{});
             }
         } else {
             uint32_t k = 0;
             for (; k + 1u < k_blocks; k += 2u, phase += 2u) {
-                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{});
-                kstep(I1{}, TRUE_{}, I0{}, ((phase + 2u) % L) * T::STAGE, FALSE_{});
+                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{});
+                kstep(I1{}, TRUE_{}, I0{}, ((phase + 2u) % L) * T::STAGE, FALSE_{}, I0{});
             }
             if (k < k_blocks) {
-                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, TRUE_{});
+                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, TRUE_{}, I0{});
                 ++phase;
             }
         }
-        epilogue();
+        if constexpr (kEpiInterleave)
+            pend = true;
+        else
+            epilogue();
+    }
+    if constexpr (kEpiInterleave) {
+        if (pend) {
+            gap_nops();  // the last tile's last MFMAs have written their accumulators
+            static_for<kEpiFirst, FM>([&](auto fm_c) __attribute__((always_inline)) {
+                static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
+                    epi_op(fm_c, t_c);
+                    store_gap();
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            });
+        }
     }
     wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
 }
