@@ -315,15 +315,19 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // stores go out in the next tile's first k-step, store t of block fm after
     // MFMA (fm - kEpiFirst)*FN + 2t, before that k-step's first MFMA on block
     // fm.  Half and half measured best: the last k-step already carries the
-    // slab barrier, most of the next slab's DMAs and its first reads.  A tile's first k-step uses the MFMA with a zero accumulator
-    // input (the k == 0 clear), so no accumulator is ever cleared by a
-    // register write.  The first tile's first k-step stores nothing (an empty
-    // store window); the last tile of a worker stores its second half after
-    // the loop.  Stores are two MFMAs apart, so a store's data registers stay
+    // slab barrier, most of the next slab's DMAs and its first reads.  A
+    // tile's first k-step uses the MFMA with a zero accumulator input (the
+    // k == 0 clear), so no accumulator is ever cleared by a register write.
+    // A worker's first tile stores nothing in its first k-step (an empty
+    // store window); its last tile stores the remaining blocks after the
+    // loop.  Stores are two MFMAs apart, so a store's data registers stay
     // intact for 32+ cycles before the next conversion (what store_gap gives
     // the plain epilogue).
     constexpr bool kEpiInterleave = TSG_EPI_INTERLEAVE && KS == 2 && EPI == 0 && WGN == 2 && FM == 8 && FN == 8;
-    constexpr int kEpiLag = 3;    // MFMAs between a block's last MFMA and its first conversion
+    // MFMAs issued between a block's last MFMA and the first read of its
+    // accumulators: the MFMAs are asm the compiler cannot see, so the wait
+    // for their results is placed here (3 MFMAs, 48+ cycles)
+    constexpr int kEpiLag = 3;
     constexpr int kEpiFirst = TSG_EPI_FIRST;  // row blocks stored in the tile's own last k-step
     static_assert(!kEpiInterleave || (kEpiFirst - 1) * FN + FN - 1 + kEpiLag + 2 * (FN / 2 - 1) < FM * FN,
                   "first-part stores must fit in the k-step");
@@ -354,8 +358,9 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     };
 
     // One 32-deep k-step: FM*FN MFMAs (fm-major) from register set CUR,
-    // accumulating into tiles that the epilogue left at zero (the k == 0
-    // clear), with the memory operations for what follows between them: the
+    // accumulating into tiles that the epilogue left at zero, or (EPH 2) from
+    // a zero accumulator input (the k == 0 clear either way), with the
+    // memory operations for what follows between them: the
     // DMAs and the reads of the next k-step into set NXT.  No read
     // into a set starts within kGap MFMAs of the last MFMA that read it: an
     // MFMA may still be fetching its operands, and a second wave on the SIMD
