@@ -69,10 +69,10 @@ __device__ __forceinline__ void mfma_mx32(f32x16& acc, i32x8 src0, i32x8 src1, u
                  : "+a"(acc) : "v"(src0), "v"(src1), "v"(s0), "v"(s1));
 }
 
-// One dword per lane from a buffer into LDS (M0 + 4 * lane).
-__device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-                 : "memory");
+// The same MFMA with a zero accumulator input (the k == 0 clear).
+__device__ __forceinline__ void mfma_mx32_clear(f32x16& acc, i32x8 src0, i32x8 src1, uint32_t s0, uint32_t s1) {
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "=a"(acc) : "v"(src0), "v"(src1), "v"(s0), "v"(s1));
 }
 
 #ifndef TSG_MX_SG
@@ -379,6 +379,53 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(set_c, r_c); });
     };
 
+    // ---- the MMA's tile scheduler and each lane's place in C ----
+    TileScheduler sched;
+    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
+    const uint32_t row0 = wr * T::WM + r, col0 = wc * T::WN + 8u * h;
+    const uint32_t lane_off = (row0 * N + col0) * 2u;
+
+    // Interleaved epilogue: a tile's C leaves between MFMAs.  Row block fm
+    // (32 rows) is final after MFMA F*fm + F-1 of the tile's last k-step.
+    // Blocks fm < kMxEpiFirst are stored in that k-step, two stores after
+    // each MFMA from F*fm + F on, so store (fn, half) reads block (fm, fn)
+    // F MFMAs after it was last written; block F-1 is final too late and is
+    // stored in the next tile's first k-step, two stores after each of its
+    // first MFMAs, long before that k-step's first MFMA on it.  That first
+    // k-step uses the MFMA with a zero accumulator input (the k == 0 clear).
+    // A worker's first tile stores nothing there (empty store window); its
+    // last tile stores block F-1 after the loop.
+    constexpr int kMxEpiFirst = F - 1;
+    static_assert(F * (kMxEpiFirst - 1) + F + F - 1 < F * F, "first-part stores must fit in the k-step");
+    __amdgpu_buffer_rsrc_t e_rc = make_rsrc(args.C, 0u);
+    uint32_t e_rows = 0, e_cols = 0;
+    // the store window of the MMA's current tile (and its trace row)
+    auto epi_state = [&]() __attribute__((always_inline)) {
+        const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
+        if (args.trace != nullptr && threadIdx.x == 0) {
+            int32_t* row = args.trace + 4 * ((size_t)wid * args.max_iters + sched.iter);
+            *(int4*)row = make_int4((int)wid, (int)sched.iter, (int)m_idx, (int)n_idx);
+            store_gap();
+        }
+        const int64_t m0 = (int64_t)m_idx * T::BM, n0 = (int64_t)n_idx * T::BN;
+        e_rows = (uint32_t)((args.M - m0) < T::BM ? (args.M - m0) : T::BM);
+        e_cols = (uint32_t)((args.N - n0) < T::BN ? (args.N - n0) : T::BN);
+        e_rc = make_rsrc(args.C + (m0 * args.N + n0), ((e_rows - 1u) * N + e_cols) * 2u);
+    };
+    // store j of row block fm: block (fm, j / 2), values 8 * (j % 2) .. + 7.
+    // Lane (h, r) of block (fm, fn) holds row 32*fm + r and columns
+    // 32*fn + 8h + 0..7 (values 0-7) and 32*fn + 16 + 8h + 0..7 (values 8-15).
+    auto epi_op = [&](auto fm_c, auto j_c) __attribute__((always_inline)) {
+        constexpr int fm = decltype(fm_c)::value, j = decltype(j_c)::value;
+        constexpr int fn = j / 2, hs = j % 2;
+        const f32x16& x = acc[fm][fn];
+        const u32x4 v = {cvt_pk<DT_BF16>(x[8 * hs + 0], x[8 * hs + 1]), cvt_pk<DT_BF16>(x[8 * hs + 2], x[8 * hs + 3]),
+                         cvt_pk<DT_BF16>(x[8 * hs + 4], x[8 * hs + 5]), cvt_pk<DT_BF16>(x[8 * hs + 6], x[8 * hs + 7])};
+        const bool ok = row0 + fm * 32 < e_rows && col0 + 32u * fn + 16u * hs < e_cols;
+        __builtin_amdgcn_raw_buffer_store_b128(v, e_rc, (ok ? lane_off : 0x80000000u) + (fn * 32 + 16 * hs) * 2,
+                                               fm * 32 * N * 2, 0);
+    };
+
     // One 64-deep k-step: 16 MFMAs (fm-major) from register set CUR, with the
     // memory operations for what follows between them: the reads of the next
     // k-step into set NXT and, in a slab's LAST k-step, the DMA of slab
@@ -387,7 +434,11 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     // the next slab's first k-step; otherwise the reads take k-step KSN of the
     // current stage.  No read into a set starts within kMxGap MFMAs of the
     // last MFMA that read it.
-    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, uint32_t read_scb) __attribute__((always_inline)) {
+    // EPH: 0 no stores, 1 the current tile's stores of blocks fm <
+    // kMxEpiFirst (its last k-step), 2 the previous tile's block F-1 (the
+    // tile's first k-step, whose MFMAs start from zero).
+    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, uint32_t read_scb, auto eph_c) __attribute__((always_inline)) {
+        constexpr int EPH = decltype(eph_c)::value;
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int NXT = 1 - CUR;
         constexpr bool LAST = decltype(last_c)::value;
@@ -412,7 +463,10 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
             constexpr int fm = s / F, fn = s % F;
             const i32x8 b8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7));
             const i32x8 a8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(fa[CUR][fm][0], fa[CUR][fm][1], 0, 1, 2, 3, 4, 5, 6, 7));
-            mfma_mx32(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
+            if constexpr (EPH == 2)
+                mfma_mx32_clear(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
+            else
+                mfma_mx32(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
             if constexpr (LAST && s == 0) slab_desc();
             if constexpr (LAST && s == ADV) slab_advance();
             if constexpr (LAST && s == S0 - 1) {
@@ -435,55 +489,23 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
                     read_op(std::integral_constant<int, NXT>{}, q_c);
                 });
             }
+            if constexpr (EPH == 1 && s >= F && s / F - 1 < kMxEpiFirst) {
+                // stores 2(s mod F), 2(s mod F) + 1 of block s / F - 1
+                epi_op(std::integral_constant<int, s / F - 1>{}, std::integral_constant<int, 2 * (s % F)>{});
+                epi_op(std::integral_constant<int, s / F - 1>{}, std::integral_constant<int, 2 * (s % F) + 1>{});
+            } else if constexpr (EPH == 2 && s < F) {
+                epi_op(std::integral_constant<int, F - 1>{}, std::integral_constant<int, 2 * s>{});
+                epi_op(std::integral_constant<int, F - 1>{}, std::integral_constant<int, 2 * s + 1>{});
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     using TRUE_ = std::integral_constant<bool, true>;
     using FALSE_ = std::integral_constant<bool, false>;
-
-    // ---- epilogue: bf16 cast and store of one finished tile, then the k == 0
-    // clear.  Lane (h, r) of block (fm, fn) holds row 32*fm + r and columns
-    // 32*fn + 8h + 0..7 (values 0-7) and 32*fn + 16 + 8h + 0..7 (values 8-15).
-    TileScheduler sched;
-    sched.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
-    const uint32_t row0 = wr * T::WM + r, col0 = wc * T::WN + 8u * h;
-    const uint32_t lane_off = (row0 * N + col0) * 2u;
-    auto epilogue = [&]() __attribute__((always_inline)) {
-        gap_nops();  // the tile's last MFMAs have written their accumulators
-        const uint32_t m_idx = sched.m_idx, n_idx = sched.n_idx;
-        if (args.trace != nullptr && threadIdx.x == 0) {
-            int32_t* row = args.trace + 4 * ((size_t)wid * args.max_iters + sched.iter);
-            *(int4*)row = make_int4((int)wid, (int)sched.iter, (int)m_idx, (int)n_idx);
-            store_gap();
-        }
-        const int64_t m0 = (int64_t)m_idx * T::BM, n0 = (int64_t)n_idx * T::BN;
-        const uint32_t rows_left = (uint32_t)((args.M - m0) < T::BM ? (args.M - m0) : T::BM);
-        const uint32_t cols_left = (uint32_t)((args.N - n0) < T::BN ? (args.N - n0) : T::BN);
-        const uint32_t c_bytes = ((rows_left - 1u) * N + cols_left) * 2u;
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(args.C + (m0 * args.N + n0), c_bytes);
-        static_for<0, F>([&](auto fm_c) __attribute__((always_inline)) {
-            constexpr int fm = decltype(fm_c)::value;
-            const bool row_ok = row0 + fm * 32 < rows_left;
-            static_for<0, F>([&](auto fn_c) __attribute__((always_inline)) {
-                constexpr int fn = decltype(fn_c)::value;
-                static_for<0, 2>([&](auto s_c) __attribute__((always_inline)) {
-                    constexpr int s = decltype(s_c)::value;
-                    const f32x16& x = acc[fm][fn];
-                    const u32x4 v = {cvt_pk<DT_BF16>(x[8 * s + 0], x[8 * s + 1]), cvt_pk<DT_BF16>(x[8 * s + 2], x[8 * s + 3]),
-                                     cvt_pk<DT_BF16>(x[8 * s + 4], x[8 * s + 5]), cvt_pk<DT_BF16>(x[8 * s + 6], x[8 * s + 7])};
-                    const bool ok = row_ok && col0 + 32u * fn + 16u * s < cols_left;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, (ok ? lane_off : 0x80000000u) + (fn * 32 + 16 * s) * 2,
-                                                           fm * 32 * N * 2, 0);
-                    store_gap();  // the store may still read its data registers
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-                acc[fm][fn] = f32x16{};
-            });
-        });
-    };
 
     // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
     for (int s = 0; s < L; ++s) {
@@ -503,18 +525,36 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     // two k-steps per slab: set 0 then set 1; the second (LAST) publishes the
     // next slab and reads its first k-step into set 0.  grp counts the scale
     // groups consumed so far exactly as the loader counts those it fetched.
+    // The k loop is rotated (the tile's first k-step, then pairs of one
+    // slab's last and the next slab's first k-step, then the tile's last
+    // k-step) so a tile is one code path and its stores can sit between the
+    // MFMAs of its last and the next tile's first k-step.
     uint32_t phase = 0, grp = 0;
+    bool pend = false;  // a tile's block F-1 is still to be stored
     for (sched.init(wid); sched.valid(); sched.next_tile()) {
-        for (uint32_t k = 0; k < k_blocks; ++k, ++phase) {
-            const uint32_t st_cur = (phase % L) * T::STAGE;
-            const uint32_t st_next = ((phase + 1u) % L) * T::STAGE;
-            const uint32_t k_next = k + 1u < k_blocks ? k + 1u : 0u;   // next slab's k (next tile at the end)
+        kstep(I0{}, FALSE_{}, I1{}, (phase % L) * T::STAGE, scale_base(grp, 0u), I2{});
+        for (uint32_t k = 0; k + 1u < k_blocks; ++k, ++phase) {
+            const uint32_t k_next = k + 1u;
             const uint32_t grp_next = grp + ((k_next % T::SG) == 0u ? 1u : 0u);
-            kstep(I0{}, FALSE_{}, I1{}, st_cur, scale_base(grp, k % T::SG));
-            kstep(I1{}, TRUE_{}, I0{}, st_next, scale_base(grp_next, k_next % T::SG));
+            kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, scale_base(grp_next, k_next % T::SG), I0{});
             grp = grp_next;
+            kstep(I0{}, FALSE_{}, I1{}, ((phase + 1u) % L) * T::STAGE, scale_base(grp, k_next % T::SG), I0{});
         }
-        epilogue();
+        // the tile's last slab: its LAST k-step reads the next tile's slab 0,
+        // which starts a scale group
+        epi_state();
+        kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, scale_base(grp + 1u, 0u), I1{});
+        grp += 1u;
+        ++phase;
+        pend = true;
+    }
+    if (pend) {
+        gap_nops();  // the last tile's last MFMAs have written their accumulators
+        static_for<0, 2 * F>([&](auto j_c) __attribute__((always_inline)) {
+            epi_op(std::integral_constant<int, F - 1>{}, j_c);
+            store_gap();  // the store may still read its data registers
+            __builtin_amdgcn_sched_barrier(0);
+        });
     }
     wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
 }
