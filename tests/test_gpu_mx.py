@@ -104,6 +104,8 @@ MX_CASES = [
     (1000, 520, 384, 3, 5, 8, False, 1),     # ragged rows and columns, odd slab count
     (300, 1032, 1024, 8, 2, 3, True, 2),     # wide scale spread, column-major, clusters of 2
     (777, 264, 256, 2, 6, 1, False, 3),      # clusters of 3 over 4 row blocks: some ranks idle
+    (768, 768, 128, 1, 2, 2, False, 1),      # one slab per tile, 4-5 tiles per worker
+    (768, 520, 256, 1, 2, 3, False, 1),      # two slabs per tile, ragged columns, 4-5 tiles per worker
 ]
 
 
