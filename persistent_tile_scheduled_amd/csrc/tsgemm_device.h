@@ -32,10 +32,10 @@ constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA i
 #define TSG_DMA_FIRST 14  // DMAs per slab issued in its first k-step of issue (0: all)
 #endif
 #ifndef TSG_EPI_INTERLEAVE
-#define TSG_EPI_INTERLEAVE 1  // 256x256 four-wave kernel: C stores between the MFMAs
+#define TSG_EPI_INTERLEAVE 1  // four-wave, 64-deep-slab kernels: C stores between the MFMAs
 #endif
 #ifndef TSG_EPI_FIRST
-#define TSG_EPI_FIRST 4  // of its 8 row blocks per wave, those stored in the tile's last k-step
+#define TSG_EPI_FIRST 4  // eighths of a wave's row blocks stored in the tile's last k-step
 #endif
 #ifndef TSG_GAP
 #define TSG_GAP 4

@@ -307,28 +307,30 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     const uint32_t row0 = wr * T::WM + l16, col0 = wc * T::WN + 8u * lg;
     const uint32_t lane_off = (row0 * N + col0) * 2u;
 
-    // Interleaved epilogue (four waves, 256x256 tiles, two k-steps per slab,
-    // direct stores): a tile's C leaves between MFMAs instead of after them.
+    // Interleaved epilogue (four waves, two k-steps per slab, direct stores:
+    // the 256x256 and 128x128 tiles with 64-deep slabs): a tile's C leaves
+    // between MFMAs instead of after them.
     // Row block fm is final after MFMA fm*FN + FN-1 of the tile's last k-step.
     // Blocks fm < kEpiFirst send each of their FN/2 stores kEpiLag + 2t MFMAs
     // later in that k-step; the rest are final too late for it, and their
     // stores go out in the next tile's first k-step, store t of block fm after
     // MFMA (fm - kEpiFirst)*FN + 2t, before that k-step's first MFMA on block
-    // fm.  Half and half measured best: the last k-step already carries the
-    // slab barrier, most of the next slab's DMAs and its first reads.  A
-    // tile's first k-step uses the MFMA with a zero accumulator input (the
-    // k == 0 clear), so no accumulator is ever cleared by a register write.
+    // fm.  Half and half (4 of 8 blocks) measured best: the last k-step
+    // already carries the slab barrier, most of the next slab's DMAs and its
+    // first reads.  A tile's first k-step uses the MFMA with a zero
+    // accumulator input (the k == 0 clear), so no accumulator is ever cleared
+    // by a register write.
     // A worker's first tile stores nothing in its first k-step (an empty
     // store window); its last tile stores the remaining blocks after the
     // loop.  Stores are two MFMAs apart, so a store's data registers stay
     // intact for 32+ cycles before the next conversion (what store_gap gives
     // the plain epilogue).
-    constexpr bool kEpiInterleave = TSG_EPI_INTERLEAVE && KS == 2 && EPI == 0 && WGN == 2 && FM == 8 && FN == 8;
+    constexpr bool kEpiInterleave = TSG_EPI_INTERLEAVE && KS == 2 && EPI == 0 && WGN == 2 && FM % 2 == 0 && FN % 2 == 0;
     // MFMAs issued between a block's last MFMA and the first read of its
     // accumulators: the MFMAs are asm the compiler cannot see, so the wait
     // for their results is placed here (3 MFMAs, 48+ cycles)
     constexpr int kEpiLag = 3;
-    constexpr int kEpiFirst = TSG_EPI_FIRST;  // row blocks stored in the tile's own last k-step
+    constexpr int kEpiFirst = TSG_EPI_FIRST * FM / 8;  // row blocks stored in the tile's own last k-step
     static_assert(!kEpiInterleave || (kEpiFirst - 1) * FN + FN - 1 + kEpiLag + 2 * (FN / 2 - 1) < FM * FN,
                   "first-part stores must fit in the k-step");
     __amdgpu_buffer_rsrc_t e_rc = make_rsrc(args.C, 0u);
