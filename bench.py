@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "cfg3_8192_bf16"
 _CSRC = "persistent_tile_scheduled_amd/csrc/"
 KERNEL_SOURCES = {
-    "gemm": tuple(_CSRC + f for f in ("tsgemm_kernel.h", "tsgemm_device.h", "tile_scheduler.h", "tsgemm.hip")),
-    "mx": tuple(_CSRC + f for f in ("tsgemm_mx_kernel.h", "tsgemm_device.h", "tile_scheduler.h", "tsgemm.hip")),
+    "gemm": tuple(_CSRC + f for f in ("tsgemm_kernel.h", "tsgemm_device.h", "tile_scheduler.h", "tsgemm_gemm_tu.hip")),
+    "mx": tuple(_CSRC + f for f in ("tsgemm_mx_kernel.h", "tsgemm_device.h", "tile_scheduler.h", "tsgemm_mx_tu.hip")),
 }
 PROFILE_FOR = {"cfg3_8192_bf16": "profiles/gemm_8192_bf16.md", "mx_8192_mxfp8": "profiles/gemm_8192_mxfp8.md"}
 
@@ -206,6 +206,8 @@ def main():
     ap.add_argument("--no-torch-context", action="store_true")
     ap.add_argument("--epilogue", type=int, choices=[0, 64], default=0,
                     help="fp16/bf16 epilogue: 0 = direct stores, 64 = C staged through LDS in 64-column chunks")
+    ap.add_argument("--series", action="store_true",
+                    help="also print every timed launch's kernel time, in launch order, to stderr")
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="MX workload: pack the scales on the device each step (default) or feed them row-major")
     args = ap.parse_args()
@@ -277,7 +279,10 @@ def main():
         launch(starts[i], ends[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    series = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if args.series:
+        print("kernel_ms in launch order: " + " ".join(f"{x:.4f}" for x in series), file=sys.stderr, flush=True)
+    launch_ms = sorted(series)
     mean_ms = sum(launch_ms) / len(launch_ms)
     if scratch is not None:
         # wall time includes the cache flushes: report the GEMM launches only

@@ -80,7 +80,7 @@ def _load():
     lib.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e8m0_decode.restype = ctypes.c_double
     lib.oracle_mx_gemm_f64.argtypes = [i64, i64, i64, u8, u8, u8, u8, d]
-    lib.oracle_mx_gemm_f64.restype = None
+    lib.oracle_mx_gemm_f64.restype = ctypes.c_int
     lib.oracle_mx_gemm_entries_f64.argtypes = [i64, u8, u8, u8, u8, i64, ctypes.POINTER(i64),
                                                ctypes.POINTER(i64), d]
     lib.oracle_mx_gemm_entries_f64.restype = None
@@ -189,12 +189,15 @@ def _mx_args(A, SFA, B, SFB):
 
 
 def mx_gemm_f64(A, SFA, B, SFB) -> np.ndarray:
-    """C64[i,j] = sum_k x(A[i,k]) s(SFA[i,k/32]) x(B[j,k]) s(SFB[j,k/32]) in binary64."""
+    """C64[i,j] = sum_k x(A[i,k]) s(SFA[i,k/32]) x(B[j,k]) s(SFB[j,k/32]) in binary64,
+    ascending k (operands decoded once; every term is exact, so the order of a
+    term's four factors does not matter)."""
     A, SFA, B, SFB, M, N, K = _mx_args(A, SFA, B, SFB)
     C = np.empty((M, N), dtype=np.float64)
     u8 = ctypes.c_uint8
-    _load().oracle_mx_gemm_f64(M, N, K, _ptr(A, u8), _ptr(SFA, u8), _ptr(B, u8), _ptr(SFB, u8),
-                               _ptr(C, ctypes.c_double))
+    if _load().oracle_mx_gemm_f64(M, N, K, _ptr(A, u8), _ptr(SFA, u8), _ptr(B, u8), _ptr(SFB, u8),
+                                  _ptr(C, ctypes.c_double)) != 0:
+        raise MemoryError("MX oracle: cannot allocate the decoded operands")
     return C
 
 

@@ -1,5 +1,6 @@
 // libtsgemm: C ABI around the persistent tile-scheduled GEMM kernels
-// (declarations and contracts: include/tsgemm.h).
+// (declarations and contracts: include/tsgemm.h).  The kernels themselves
+// are compiled in their own translation units (tsgemm_launch.h).
 //
 // Host conventions follow the lowered host code on page "tilelang" (blog,
 // section 1.3): argument checks before any launch, 0 / negative return codes,
@@ -16,12 +17,37 @@
 
 #include "tsgemm.h"
 #include "tile_scheduler.h"
-#include "tsgemm_kernel.h"
+#include "tsgemm_launch.h"
 #include "tsgemm_mx_kernel.h"
+
+namespace tsg {
+
+// C = 0 when K == 0 (an empty sum): plain 16-byte stores, N % 8 == 0.
+__global__ void tsgemm_zero_kernel(uint16_t* C, int64_t count8) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count8) *(u32x4*)(C + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Schedule dump: the same scheduler and worker numbering as the GEMM kernel.
+__global__ void tsgemm_schedule_kernel(uint32_t P, uint32_t m_blocks, uint32_t n_blocks,
+                                       uint32_t group, uint32_t cluster, uint32_t col_major,
+                                       uint32_t num_xcd, uint32_t max_iters, int32_t* out) {
+    if (threadIdx.x != 0) return;
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, P, num_xcd);
+    TileScheduler s;
+    s.setup(P, m_blocks, n_blocks, group, cluster, col_major);
+    for (s.init(wid); s.valid(); s.next_tile()) {
+        int32_t* row = out + 4 * ((size_t)wid * max_iters + s.iter);
+        *(int4*)row = make_int4((int)wid, (int)s.iter, (int)s.m_idx, (int)s.n_idx);
+    }
+}
+
+}  // namespace tsg
 
 namespace {
 
-constexpr int kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
+using tsg::KernelEntry;
+using tsg::kLdsBytes;
 constexpr int kMaxSlots = 5;           // deepest compiled LDS ring
 
 thread_local char g_err[512] = "";
@@ -34,33 +60,28 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
-typedef void (*launch_fn)(const tsg::GemmArgs&, unsigned grid, hipStream_t);
+// Every compiled fp16/bf16 kernel, gathered from the translation units that
+// build them (one per dtype and tile shape).
+struct KernelTable {
+    std::vector<KernelEntry> entries;
+    KernelTable() {
+        typedef const KernelEntry* (*tu_fn)(int*);
+        const tu_fn tus[] = {tsg::TSG_GEMM_TU_FN(1, 128, 32), tsg::TSG_GEMM_TU_FN(1, 128, 64),
+                             tsg::TSG_GEMM_TU_FN(1, 256, 32), tsg::TSG_GEMM_TU_FN(1, 256, 64),
+                             tsg::TSG_GEMM_TU_FN(2, 128, 32), tsg::TSG_GEMM_TU_FN(2, 128, 64),
+                             tsg::TSG_GEMM_TU_FN(2, 256, 32), tsg::TSG_GEMM_TU_FN(2, 256, 64)};
+        for (tu_fn f : tus) {
+            int n = 0;
+            const KernelEntry* e = f(&n);
+            entries.insert(entries.end(), e, e + n);
+        }
+    }
+};
 
-template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI>
-void launch(const tsg::GemmArgs& a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((tsg::tsgemm_kernel<DT, BM, BN, BK, L, WGN, EPI>), dim3(grid), dim3(64 * 2 * WGN), 0, s, a);
+const std::vector<KernelEntry>& kernels() {
+    static const KernelTable table;  // thread-safe one-time construction
+    return table.entries;
 }
-
-struct KernelEntry {
-    int dt, bm, bn, bk, slots, waves, epi;
-    launch_fn fn;
-};
-
-// LDS of `S` ring slots plus the chunked epilogue's buffer fits?  Entries whose
-// slot count does not fit are compiled with 2 slots and never selected.
-#define TSG_FIT(BM, BN, BK, S, EPI) (((BM * BK + BK * BN) * 2 * S + BM * EPI * 2) <= kLdsBytes)
-#define TSG_SLOTS(DT, BM, BN, BK, WGN, EPI)                                                                 \
-    {DT, BM, BN, BK, 2, 2 * WGN, EPI, launch<DT, BM, BN, BK, 2, WGN, EPI>},                                 \
-    {DT, BM, BN, BK, 3, 2 * WGN, EPI, launch<DT, BM, BN, BK, TSG_FIT(BM, BN, BK, 3, EPI) ? 3 : 2, WGN, EPI>}, \
-    {DT, BM, BN, BK, 4, 2 * WGN, EPI, launch<DT, BM, BN, BK, TSG_FIT(BM, BN, BK, 4, EPI) ? 4 : 2, WGN, EPI>}, \
-    {DT, BM, BN, BK, 5, 2 * WGN, EPI, launch<DT, BM, BN, BK, TSG_FIT(BM, BN, BK, 5, EPI) ? 5 : 2, WGN, EPI>}
-#define TSG_TILE(DT, BM, BN, BK) \
-    TSG_SLOTS(DT, BM, BN, BK, 2, 0), TSG_SLOTS(DT, BM, BN, BK, 4, 0), TSG_SLOTS(DT, BM, BN, BK, 2, 64)
-
-const KernelEntry kKernels[] = {
-    TSG_TILE(1, 128, 128, 32), TSG_TILE(1, 128, 128, 64), TSG_TILE(1, 256, 256, 32), TSG_TILE(1, 256, 256, 64),
-    TSG_TILE(2, 128, 128, 32), TSG_TILE(2, 128, 128, 64), TSG_TILE(2, 256, 256, 32), TSG_TILE(2, 256, 256, 64),
-};
 
 // Default wavefronts per workgroup for a tile shape (measured on MI355X).
 int default_waves(int bm, int bn, int bk) {
@@ -69,7 +90,7 @@ int default_waves(int bm, int bn, int bk) {
 }
 
 const KernelEntry* find_kernel(int dt, int bm, int bn, int bk, int slots, int waves, int epi) {
-    for (const KernelEntry& e : kKernels)
+    for (const KernelEntry& e : kernels())
         if (e.dt == dt && e.bm == bm && e.bn == bn && e.bk == bk && e.slots == slots && e.waves == waves &&
             e.epi == epi)
             return &e;
@@ -257,12 +278,7 @@ int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void
         a.cluster = (uint32_t)p->cluster;
         a.col_major = (uint32_t)p->col_major;
         a.n_groups = mx_groups(p);
-        if (packed)
-            hipLaunchKernelGGL(tsg::tsgemm_mx_kernel<true>, dim3(g.P), dim3(tsg::MxTraits::THREADS), 0,
-                               static_cast<hipStream_t>(stream), a);
-        else
-            hipLaunchKernelGGL(tsg::tsgemm_mx_kernel<false>, dim3(g.P), dim3(tsg::MxTraits::THREADS), 0,
-                               static_cast<hipStream_t>(stream), a);
+        tsg::launch_mx(a, g.P, packed, static_cast<hipStream_t>(stream));
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TSGEMM_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -430,9 +446,9 @@ int tsgemm_mx_pack_scales(const tsgemm_plan* p, int operand, const void* SF, voi
     const int64_t blocks = operand == 0 ? p->m_blocks : p->n_blocks;
     const int64_t dwords = bytes / 4;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(tsg::tsgemm_mx_pack_kernel, dim3((unsigned)((dwords + 255) / 256)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(SF), static_cast<uint8_t*>(SFP),
-                       rows, (uint32_t)(p->K / 32), (uint32_t)blocks, mx_groups(p));
+    tsg::launch_mx_pack(static_cast<const uint8_t*>(SF), static_cast<uint8_t*>(SFP), rows, (uint32_t)(p->K / 32),
+                        (uint32_t)blocks, mx_groups(p), (unsigned)((dwords + 255) / 256),
+                        static_cast<hipStream_t>(stream));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TSGEMM_EHIP, "pack kernel launch failed: %s", hipGetErrorString(e));
     return TSGEMM_OK;

@@ -645,24 +645,4 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
 }
 
-// C = 0 when K == 0 (an empty sum): plain 16-byte stores, N % 8 == 0.
-__global__ void tsgemm_zero_kernel(uint16_t* C, int64_t count8) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < count8) *(u32x4*)(C + 8 * i) = u32x4{0u, 0u, 0u, 0u};
-}
-
-// Schedule dump: the same scheduler and worker numbering as the GEMM kernel.
-__global__ void tsgemm_schedule_kernel(uint32_t P, uint32_t m_blocks, uint32_t n_blocks,
-                                       uint32_t group, uint32_t cluster, uint32_t col_major,
-                                       uint32_t num_xcd, uint32_t max_iters, int32_t* out) {
-    if (threadIdx.x != 0) return;
-    const uint32_t wid = worker_of_workgroup(blockIdx.x, P, num_xcd);
-    TileScheduler s;
-    s.setup(P, m_blocks, n_blocks, group, cluster, col_major);
-    for (s.init(wid); s.valid(); s.next_tile()) {
-        int32_t* row = out + 4 * ((size_t)wid * max_iters + s.iter);
-        *(int4*)row = make_int4((int)wid, (int)s.iter, (int)s.m_idx, (int)s.n_idx);
-    }
-}
-
 }  // namespace tsg

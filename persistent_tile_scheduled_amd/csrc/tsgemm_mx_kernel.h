@@ -559,26 +559,4 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
 }
 
-// Scale packing for the PACKED kernel: SF[rows][K/32] (row-major E8M0) ->
-// SFP[block][group][256][SC_ROW], block = 256-row block, group = SG consecutive
-// 128-deep slabs (SC_ROW = 4 * SG bytes of one row).  Rows past `rows` and
-// bytes past K/32 are written as 0.  One thread per output dword.
-__global__ void tsgemm_mx_pack_kernel(const uint8_t* SF, uint8_t* SFP, int64_t rows, uint32_t kb_bytes,
-                                      uint32_t blocks, uint32_t n_groups) {
-    constexpr uint32_t DW = MxTraits::SC_ROW / 4;  // dwords per row and group
-    const uint64_t total = (uint64_t)blocks * n_groups * MxTraits::BM * DW;
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= total) return;
-    const uint32_t d = (uint32_t)(t % DW);
-    const uint64_t rg = t / DW;                    // ((block * n_groups + group) * 256 + r)
-    const uint32_t r = (uint32_t)(rg % MxTraits::BM);
-    const uint64_t bg = rg / MxTraits::BM;
-    const uint32_t g = (uint32_t)(bg % n_groups), blk = (uint32_t)(bg / n_groups);
-    const int64_t row = (int64_t)blk * MxTraits::BM + r;
-    const uint32_t col = g * (uint32_t)MxTraits::SC_ROW + d * 4u;   // byte within the row, multiple of 4
-    uint32_t v = 0;
-    if (row < rows && col < kb_bytes) v = *(const uint32_t*)(SF + row * kb_bytes + col);  // kb_bytes % 4 == 0
-    *(uint32_t*)(SFP + t * 4) = v;
-}
-
 }  // namespace tsg

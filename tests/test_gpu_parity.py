@@ -4,9 +4,9 @@ Tolerance (from the problem statement of the persistent tile-scheduled GEMM):
 elementwise |C - Cref| <= 2e-3 * (|Cref| + 1) and relative Frobenius error
 <= 1e-3, with Cref the oracle's fp64 sum rounded once to the output dtype.
 Schedules (device dump and the GEMM kernel's own trace) must match the oracle
-bit for bit.  Sizes the oracle finishes in seconds are compared element by
-element; the full-size shapes are compared on sampled outputs computed one by
-one, plus whole-matrix properties (every element written, guard bands intact).
+bit for bit.  Every shape, the four large benchmark shapes included, is
+compared element by element against the oracle's whole product, with the
+Frobenius criterion taken over all of C; guard bands after C must stay intact.
 """
 
 import numpy as np
@@ -267,49 +267,52 @@ def test_gemm_kernel_trace_matches_oracle(cfg, waves):
     assert np.array_equal(rows, want)
 
 
-# ---------------------------------------------------------------- full size, sampled
-def _sampled_check(w, n_samples=6000, seed=9, waves=0):
-    A, B = workload_inputs(w)
-    plan = _plan_for(w, waves)
-    guard = 4096
-    C, g = _run(plan, A, B, w.dtype, guard=guard)
-    assert torch.isnan(g.float()).all(), "write past the end of C"
-    Cf = C.float()
-    assert torch.isfinite(Cf).all(), "unwritten or non-finite outputs"
-    rng = np.random.default_rng(seed)
-    rows = rng.integers(0, w.M, n_samples)
-    cols = rng.integers(0, w.N, n_samples)
-    # plus the last row and column (ragged tails) and tile corners
-    edge_r = np.concatenate([np.full(256, w.M - 1), rng.integers(0, w.M, 256)])
-    edge_c = np.concatenate([rng.integers(0, w.N, 256), np.full(256, w.N - 1)])
-    rows = np.concatenate([rows, edge_r, [0, w.M - 1, 0, w.M - 1]])
-    cols = np.concatenate([cols, edge_c, [0, 0, w.N - 1, w.N - 1]])
-    A64, B64 = A.double().numpy(), B.double().numpy()
-    c64 = oracle.gemm_entries_f64(A64, B64, rows, cols)
-    ref = _bits_to_f64(oracle.round_to(c64, FMT[w.dtype]), w.dtype)
-    got = C.double().numpy()[rows, cols]
-    return _check_close(got, ref, w.name)
+# ---------------------------------------------------------------- full size, every element
+_FULL_REF = {}
 
 
+def _full_reference(cfg):
+    """Inputs and the oracle's whole C (rounded once to the dtype, as binary64)
+    of one benchmark shape; the last shape asked for is kept, so the wave
+    counts of one shape share one oracle run."""
+    if cfg not in _FULL_REF:
+        _FULL_REF.clear()
+        w = WORKLOADS[cfg]
+        A, B = workload_inputs(w)
+        ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[w.dtype])
+        _FULL_REF[cfg] = (A, B, _bits_to_f64(ref_bits, w.dtype))
+    return _FULL_REF[cfg]
+
+
+def _row_col_fro(got, ref):
+    """Largest relative Frobenius error of any single row and of any single column."""
+    d2 = (got - ref) ** 2
+    r2 = ref ** 2
+    row = np.sqrt(d2.sum(axis=1) / np.maximum(r2.sum(axis=1), 1e-300)).max()
+    col = np.sqrt(d2.sum(axis=0) / np.maximum(r2.sum(axis=0), 1e-300)).max()
+    return row, col
+
+
+@pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("cfg", ["cfg3_8192_bf16", "cfg4_16384x4096x4096_fp16",
                                  "cfg4p_16000x4000x4096_fp16", "cfg5_2048x2048x32768_bf16"])
-@pytest.mark.parametrize("waves", [4, 8])
-def test_full_size_sampled(cfg, waves):
+def test_full_size_every_element(cfg, waves):
+    """The four large shapes in the benchmarked launch configuration (one
+    workgroup per CU, XCD remap on), 4 and 8 waves: every element of C against
+    the oracle's whole product under both criteria (elementwise bound and
+    relative Frobenius error over all of C), and nothing written past C."""
+    w = WORKLOADS[cfg]
     print(f"[case] full {cfg} waves={waves}", flush=True)
-    _sampled_check(WORKLOADS[cfg], waves=waves)
-
-
-def test_full_tile_of_8192_exact_compare():
-    """One whole 256x256 output tile of the 8192^3 shape, every element."""
-    w = WORKLOADS["cfg3_8192_bf16"]
-    print("[case] cfg3 tile", flush=True)
-    A, B = workload_inputs(w)
-    plan = _plan_for(w)
-    C, _ = _run(plan, A, B, w.dtype)
-    r0, c0 = 256 * 17, 256 * 29
-    ref_bits, _ = oracle.reference_c(A[r0:r0 + 256].double().numpy(), B[:, c0:c0 + 256].double().numpy(),
-                                     FMT[w.dtype])
-    _check_close(C[r0:r0 + 256, c0:c0 + 256].double().numpy(), _bits_to_f64(ref_bits, w.dtype), "cfg3 tile")
+    A, B, ref = _full_reference(cfg)
+    plan = _plan_for(w, waves)
+    C, g = _run(plan, A, B, w.dtype, guard=4096)
+    assert torch.isnan(g.float()).all(), "write past the end of C"
+    got = C.double().numpy()
+    err_max, fro = _check_close(got, ref, f"{cfg} waves={waves}")
+    worst = (np.abs(got - ref) / (2e-3 * (np.abs(ref) + 1.0))).max()
+    row, col = _row_col_fro(got, ref)
+    print(f"  max |err| {err_max:.3g}, worst err/bound {worst:.3g}, rel. Frobenius {fro:.3g}, "
+          f"worst row {row:.3g}, worst column {col:.3g}", flush=True)
 
 
 def test_deterministic_repeat():

@@ -130,6 +130,25 @@ def test_entries_match_full_product():
     assert np.array_equal(oracle.mx_gemm_entries_f64(A, SA, B, SB, rows, cols), full[rows, cols])
 
 
+def test_decoded_product_equals_term_by_term_sums():
+    """The full product decodes each operand once and sums in i-k-j order; the
+    per-entry routine multiplies the four factors of every term as it goes.
+    Every term is exact in binary64, so both must give the same bits (NaN
+    blocks, negative-zero rows and a wide spread of scales included)."""
+    from workloads import make_mx_inputs
+    A, SFA, B, SFB = make_mx_inputs(40, 36, 512, seed=11, spread=30)
+    A[3, 7] = 0x7F
+    SFB[5, 2] = 0xFF
+    A[9, :] = 0x80
+    full = oracle.mx_gemm_f64(A, SFA, B, SFB)
+    r, c = np.meshgrid(np.arange(40), np.arange(36), indexing="ij")
+    each = oracle.mx_gemm_entries_f64(A, SFA, B, SFB, r.ravel(), c.ravel()).reshape(40, 36)
+    assert np.array_equal(np.isnan(full), np.isnan(each))
+    fin = ~np.isnan(full)
+    assert np.isnan(full[3]).all() and np.isnan(full[:, 5]).all() and fin.sum() > 0
+    assert np.array_equal(full[fin].view(np.uint64), each[fin].view(np.uint64))
+
+
 def test_shape_checks():
     with pytest.raises(ValueError):
         oracle.mx_gemm_f64(np.zeros((2, 48), np.uint8), np.zeros((2, 1), np.uint8),
