@@ -77,7 +77,12 @@ typedef struct tsgemm_info {
 
 /*
  * Validate a problem and build a plan.  Returns NULL on error (message in
- * tsgemm_last_error()).  Makes no HIP call.
+ * tsgemm_last_error(), code in tsgemm_last_error_code()).  Makes no HIP call.
+ * Defined by the host side of the persistent example (page "[Feature]
+ * Introduce tile scheduler #2441", Files changed, gemm_persistent: m_blocks =
+ * ceildiv(M, block_M), n_blocks = ceildiv(N, block_N), the worker count and
+ * the K % block_K assertion) and by the argument checks of the lowered host
+ * function (page "tilelang", section 1.3).
  *   M, N, K      >= 0; K % block_K == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows,
  *                as the lowered host function's "divisible by 8" check);
  *                block_M*K*2, block_K*N*2 and block_M*N*2 below 2^31 (per-tile
@@ -132,7 +137,11 @@ int tsgemm_set_epilogue(tsgemm_plan* plan, int store_block_N);
 int tsgemm_set_xcd_remap(tsgemm_plan* plan, int enable);
 
 /* Asynchronously compute C = A*B on `stream` (a hipStream_t; NULL = default
- * stream).  A, B, C: device pointers, 16-byte aligned, holding M*K, K*N and
+ * stream).  The launch of page "tilelang" section 1.3 (call(A, B, C, stream):
+ * one kernel on the caller's stream, 0 or an error code back); the product
+ * and its persistent loop are those of page "[Feature] Introduce tile
+ * scheduler #2441", Files changed, gemm_persistent (slabs of A and B staged
+ * in shared memory, fp32 accumulation, cast and store per tile).  A, B, C: device pointers, 16-byte aligned, holding M*K, K*N and
  * M*N elements; C is fully overwritten and must not overlap A or B.  Buffers
  * must stay alive until the stream work completes.  M*N == 0 launches nothing. */
 int tsgemm_run(const tsgemm_plan* plan, const void* A, const void* B, void* C, void* stream);
@@ -198,25 +207,51 @@ int tsgemm_mx_pack_scales(const tsgemm_plan* plan, int operand, const void* SF, 
 int tsgemm_run_mx_packed(const tsgemm_plan* plan, const void* A, const void* SFAP, const void* B,
                          const void* SFBP, void* C, void* stream);
 
-int64_t tsgemm_num_tiles(const tsgemm_plan* plan);       /* < 0 on error                */
+/* m_blocks * n_blocks, the tile count the scheduler walks (page "[Feature]
+ * Introduce tile scheduler #2441", Files changed: the waves formula
+ * ceildiv(m_blocks * n_blocks, sm_num)); < 0 on error. */
+int64_t tsgemm_num_tiles(const tsgemm_plan* plan);
 int tsgemm_num_workgroups(const tsgemm_plan* plan);      /* resolves the default P      */
 int tsgemm_plan_info(const tsgemm_plan* plan, tsgemm_info* info);
+
+/* The launch geometry tsgemm_run would use on the current device: the number
+ * of workgroups P (the explicit one, or one per compute unit), the waves of
+ * the busiest worker (max_iters: a traced run writes P * max_iters rows) and
+ * the XCD count the worker renumbering uses (1 when it is off).  Any output
+ * pointer may be NULL.  Queries device attributes only for what the plan
+ * leaves to the device (the default P; the XCD count when num_xcds is asked
+ * for and the renumbering is on); launches nothing. */
+int tsgemm_launch_info(const tsgemm_plan* plan, int32_t* num_workgroups, int32_t* max_iters,
+                       int32_t* num_xcds);
 
 /* Run the scheduler on the device over the plan's persistent grid and write
  * num_tiles rows of int32 (worker, iter, m_idx, n_idx), sorted by
  * (worker, iter), to the HOST buffer `out` (4 * num_tiles int32).
- * Synchronous (default stream). */
+ * Synchronous (default stream); allocates and frees a device buffer of
+ * 16 * P * max_iters bytes.  The scheduler is the one page "[Feature]
+ * Introduce tile scheduler #2441" describes (Conversation tab, overview of
+ * tile_schedule.py: init(worker), valid(), next_tile(), m_idx / n_idx and the
+ * iteration counter current_iter; Files changed: the manual walk it replaces,
+ * tile_id = sm_num * w + worker decoded in groups of group_size columns). */
 int tsgemm_dump_schedule(const tsgemm_plan* plan, int32_t* out);
 
 /* The same rows computed on the host by the same scheduler code compiled for
  * the CPU, for `num_workgroups` workers (> 0).  Makes no HIP call. */
 int tsgemm_schedule_host(const tsgemm_plan* plan, int num_workgroups, int32_t* out);
 
-void tsgemm_destroy(tsgemm_plan* plan);                  /* NULL-safe */
+/* Free a plan (host memory only; it holds no device resource).  NULL-safe.
+ * The pages' host stubs (page "tilelang", section 1.3) keep their state in
+ * statics and have no teardown; a plan here is an explicit object instead. */
+void tsgemm_destroy(tsgemm_plan* plan);
 
 /* Message of the last failing call on this thread ("" if none).  Valid until
- * the next tsgemm call on the same thread. */
+ * the next tsgemm call on the same thread (page "tilelang", section 1.3:
+ * get_last_error() returning the text kept by the failing call). */
 const char* tsgemm_last_error(void);
+
+/* TSGEMM_E* code of the last failing call on this thread (TSGEMM_OK if the
+ * last call succeeded); for calls that return NULL rather than a code. */
+int tsgemm_last_error_code(void);
 
 #ifdef __cplusplus
 }

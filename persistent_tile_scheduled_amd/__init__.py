@@ -34,6 +34,7 @@ EXPORTS = (
     "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_mx_packed_scale_bytes",
     "tsgemm_mx_pack_scales", "tsgemm_run_mx_packed", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
+    "tsgemm_last_error_code", "tsgemm_launch_info",
 )
 
 
@@ -117,6 +118,10 @@ def load(path: str | None = None):
     lib.tsgemm_destroy.restype = None
     lib.tsgemm_last_error.argtypes = []
     lib.tsgemm_last_error.restype = ctypes.c_char_p
+    lib.tsgemm_last_error_code.argtypes = []
+    lib.tsgemm_last_error_code.restype = i32
+    lib.tsgemm_launch_info.argtypes = [vp, i32p, i32p, i32p]
+    lib.tsgemm_launch_info.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -149,9 +154,7 @@ class Plan:
             dt = {torch.float16: FP16, torch.bfloat16: BF16}.get(dtype, 0)
         h = lib.tsgemm_create(M, N, K, dt, block_M, block_N, block_K, group_size, num_stages)
         if not h:
-            msg = last_error()
-            raise TsgemmError(EUNSUPPORTED if "compiled" in msg or "fit" in msg or "exceeds" in msg
-                              else EINVAL, msg)
+            raise TsgemmError(lib.tsgemm_last_error_code(), last_error())
         self._h = ctypes.c_void_p(h)
         self.M, self.N, self.K, self.dtype = M, N, K, dt
         if num_workgroups:
@@ -196,15 +199,17 @@ class Plan:
         _check(self._lib.tsgemm_dump_schedule(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
         return out
 
+    def launch_info(self) -> dict:
+        """tsgemm_launch_info: the grid a run uses on the current device."""
+        P, it, x = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.tsgemm_launch_info(self._h, ctypes.byref(P), ctypes.byref(it), ctypes.byref(x)))
+        return {"num_workgroups": P.value, "max_iters": it.value, "num_xcds": x.value}
+
     def trace_rows(self) -> int:
-        """Rows (of 4 int32) a traced run may write: P * max_iters for the
-        plan's resolved number of workgroups P and cluster size cs."""
-        inf = self.info()
-        P, cs = self.num_workgroups, inf["cluster_size"]
-        if P % cs:
-            raise TsgemmError(EINVAL, f"the {P} workgroups do not split into clusters of {cs}")
-        m_cl = -(-inf["m_blocks"] // cs)
-        return P * (-(-(m_cl * inf["n_blocks"]) // (P // cs)))
+        """Rows (of 4 int32) a traced run may write: P * max_iters."""
+        P, it = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.tsgemm_launch_info(self._h, ctypes.byref(P), ctypes.byref(it), None))
+        return P.value * it.value
 
     def _check_trace(self, trace):
         import torch

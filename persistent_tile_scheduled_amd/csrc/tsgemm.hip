@@ -51,12 +51,20 @@ using tsg::kLdsBytes;
 constexpr int kMaxSlots = 5;           // deepest compiled LDS ring
 
 thread_local char g_err[512] = "";
+thread_local int g_code = 0;
+
+// Every entry point starts by clearing the last error of its thread.
+void reset_error() {
+    g_err[0] = '\0';
+    g_code = 0;
+}
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
     va_end(ap);
+    g_code = code;
     return code;
 }
 
@@ -112,23 +120,37 @@ bool tile_supported(int bm, int bn, int bk) {
            (bm == 256 && bn == 256 && (bk == 32 || bk == 64));
 }
 
-// Persistent grid default: one workgroup per compute unit of the device.
+// Persistent grid default: one workgroup per compute unit of the device; the
+// XCD count (accelerator complex dies, each with its own L2) drives the
+// worker renumbering.  Both are queried once per device and cached.
 std::atomic<int> g_cu_count[64];
+std::atomic<int> g_xcd_count[64];
 
 int device_cus(int* cus, int* xcds) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(TSGEMM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-    int n = (dev >= 0 && dev < 64) ? g_cu_count[dev].load() : 0;
-    if (n <= 0) {
+    const bool cached = dev >= 0 && dev < 64;
+    int n = cached ? g_cu_count[dev].load() : 0;
+    int x = cached ? g_xcd_count[dev].load() : 0;
+    if (n <= 0 || x <= 0) {
         e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess || n <= 0)
             return fail(TSGEMM_EHIP, "cannot query the compute-unit count: %s", hipGetErrorString(e));
-        if (dev >= 0 && dev < 64) g_cu_count[dev].store(n);
+        // Workgroup b of a launch goes to XCD b % (XCD count).  A runtime that
+        // cannot report the count gets 1: the renumbering is then the
+        // identity, which changes speed only, never C or the schedule.
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0) {
+            (void)hipGetLastError();
+            x = 1;
+        }
+        if (cached) {
+            g_cu_count[dev].store(n);
+            g_xcd_count[dev].store(x);
+        }
     }
     *cus = n;
-    // MI300-class parts expose 8 XCDs per device in single-partition mode.
-    *xcds = n >= 128 ? 8 : 1;
+    *xcds = x;
     return TSGEMM_OK;
 }
 
@@ -183,7 +205,7 @@ int resolve_grid(const tsgemm_plan* p, Grid* g) {
 }
 
 int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* stream, int32_t* trace) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (is_mx(p)) return fail(TSGEMM_EINVAL, "an MXFP8 plan runs with tsgemm_run_mx");
     if (p->M == 0 || p->N == 0) return TSGEMM_OK;  // empty output: nothing to launch
@@ -237,7 +259,7 @@ int64_t mx_packed_bytes(const tsgemm_plan* p, int64_t blocks) {
 
 int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB, void* C,
                 void* stream, int32_t* trace, bool packed) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (!is_mx(p)) return fail(TSGEMM_EINVAL, "tsgemm_run_mx needs a TSGEMM_MXFP8 plan (dtype %d)", p->dtype);
     if (p->M == 0 || p->N == 0) return TSGEMM_OK;
@@ -291,9 +313,11 @@ extern "C" {
 
 const char* tsgemm_last_error(void) { return g_err; }
 
+int tsgemm_last_error_code(void) { return g_code; }
+
 tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block_M, int block_N,
                            int block_K, int group_size, int num_stages) {
-    g_err[0] = '\0';
+    reset_error();
     if (M < 0 || N < 0 || K < 0) { fail(TSGEMM_EINVAL, "M, N, K must be >= 0"); return nullptr; }
     if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) {
         fail(TSGEMM_EINVAL, "M, N and K must be below 2^31"); return nullptr;
@@ -351,7 +375,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
 }
 
 int tsgemm_set_num_workgroups(tsgemm_plan* p, int num_workgroups) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (num_workgroups < 0) return fail(TSGEMM_EINVAL, "num_workgroups must be >= 0");
     p->P = num_workgroups;
@@ -359,7 +383,7 @@ int tsgemm_set_num_workgroups(tsgemm_plan* p, int num_workgroups) {
 }
 
 int tsgemm_set_waves(tsgemm_plan* p, int waves) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (waves == 0) waves = default_waves(p->bm, p->bn, p->bk);
     if (waves != 4 && waves != 8) return fail(TSGEMM_EINVAL, "waves must be 0, 4 or 8, got %d", waves);
@@ -372,7 +396,7 @@ int tsgemm_set_waves(tsgemm_plan* p, int waves) {
 }
 
 int tsgemm_set_epilogue(tsgemm_plan* p, int store_block_N) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (store_block_N != 0 && store_block_N != 64)
         return fail(TSGEMM_EINVAL, "store_block_N must be 0 (direct stores) or 64, got %d", store_block_N);
@@ -389,7 +413,7 @@ int tsgemm_set_epilogue(tsgemm_plan* p, int store_block_N) {
 }
 
 int tsgemm_set_xcd_remap(tsgemm_plan* p, int enable) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (enable != 0 && enable != 1) return fail(TSGEMM_EINVAL, "enable must be 0 or 1");
     p->xcd_remap = enable;
@@ -397,7 +421,7 @@ int tsgemm_set_xcd_remap(tsgemm_plan* p, int enable) {
 }
 
 int tsgemm_set_schedule(tsgemm_plan* p, int column_major, int cluster_size) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (column_major != 0 && column_major != 1) return fail(TSGEMM_EINVAL, "column_major must be 0 or 1");
     if (cluster_size < 1 || cluster_size > 64) return fail(TSGEMM_EINVAL, "cluster_size must be in [1, 64], got %d", cluster_size);
@@ -428,7 +452,7 @@ int tsgemm_run_mx_traced(const tsgemm_plan* p, const void* A, const void* SFA, c
 }
 
 int64_t tsgemm_mx_packed_scale_bytes(const tsgemm_plan* p, int operand) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (!is_mx(p)) return fail(TSGEMM_EINVAL, "not a TSGEMM_MXFP8 plan (dtype %d)", p->dtype);
     if (operand != 0 && operand != 1) return fail(TSGEMM_EINVAL, "operand must be 0 (SFA) or 1 (SFB), got %d", operand);
@@ -460,13 +484,13 @@ int tsgemm_run_mx_packed(const tsgemm_plan* p, const void* A, const void* SFAP, 
 }
 
 int64_t tsgemm_num_tiles(const tsgemm_plan* p) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     return p->tiles;
 }
 
 int tsgemm_num_workgroups(const tsgemm_plan* p) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (p->P) return p->P;
     int cus = 0, xcds = 1;
@@ -474,8 +498,27 @@ int tsgemm_num_workgroups(const tsgemm_plan* p) {
     return rc != TSGEMM_OK ? rc : cus;
 }
 
+int tsgemm_launch_info(const tsgemm_plan* p, int32_t* num_workgroups, int32_t* max_iters, int32_t* num_xcds) {
+    reset_error();
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    // the device is consulted only for what the plan leaves to it: the
+    // default worker count, and the XCD count when asked for
+    int cus = 0, xcds = 1;
+    if (p->P == 0 || (num_xcds && p->xcd_remap)) {
+        int rc = device_cus(&cus, &xcds);
+        if (rc != TSGEMM_OK) return rc;
+    }
+    const uint32_t P = (uint32_t)(p->P ? p->P : cus);
+    if (P % (uint32_t)p->cluster != 0)
+        return fail(TSGEMM_EINVAL, "the %u workgroups do not split into clusters of %d", P, p->cluster);
+    if (num_workgroups) *num_workgroups = (int32_t)P;
+    if (max_iters) *max_iters = (int32_t)max_iters_for(p, P);
+    if (num_xcds) *num_xcds = p->xcd_remap ? (int32_t)xcds : 1;
+    return TSGEMM_OK;
+}
+
 int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p || !info) return fail(TSGEMM_EINVAL, "plan or info is NULL");
     std::memset(info, 0, sizeof(*info));
     info->M = p->M; info->N = p->N; info->K = p->K;
@@ -499,7 +542,7 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
 }
 
 int tsgemm_schedule_host(const tsgemm_plan* p, int num_workgroups, int32_t* out) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p || !out) return fail(TSGEMM_EINVAL, "plan or out is NULL");
     if (num_workgroups <= 0) return fail(TSGEMM_EINVAL, "num_workgroups must be > 0");
     if (num_workgroups % p->cluster != 0)
@@ -520,7 +563,7 @@ int tsgemm_schedule_host(const tsgemm_plan* p, int num_workgroups, int32_t* out)
 }
 
 int tsgemm_dump_schedule(const tsgemm_plan* p, int32_t* out) {
-    g_err[0] = '\0';
+    reset_error();
     if (!p || !out) return fail(TSGEMM_EINVAL, "plan or out is NULL");
     if (p->tiles == 0) return TSGEMM_OK;
     Grid g;

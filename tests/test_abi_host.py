@@ -52,6 +52,35 @@ def test_create_rejects(args, code, needle):
     h = lib.tsgemm_create(*args)
     assert not h
     assert needle in tsg.last_error()
+    assert lib.tsgemm_last_error_code() == code
+    with pytest.raises(tsg.TsgemmError) as e:
+        tsg.Plan(*args)
+    assert e.value.code == code
+
+
+def test_error_code_clears_on_success():
+    lib = tsg.load()
+    assert not lib.tsgemm_create(512, 512, 512, 9, 128, 128, 64, 2, 2)
+    assert lib.tsgemm_last_error_code() == tsg.EINVAL
+    h = lib.tsgemm_create(512, 512, 512, 1, 128, 128, 64, 2, 2)
+    assert h and lib.tsgemm_last_error_code() == tsg.OK and tsg.last_error() == ""
+    lib.tsgemm_destroy(h)
+
+
+@pytest.mark.parametrize("cs", [1, 2, 3])
+def test_launch_info_explicit_grid_needs_no_device(cs):
+    """With an explicit worker count the grid comes from the plan alone: P and
+    the busiest worker's waves ceil(ceil(m_blocks/cs) * n_blocks / (P/cs))."""
+    p = tsg.Plan(7 * 128 - 40, 6 * 128, 256, "fp16", 128, 128, 64, 4, 2, num_workgroups=6 * cs, cluster_size=cs)
+    lib = tsg.load()
+    P, it = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.tsgemm_launch_info(p._h, ctypes.byref(P), ctypes.byref(it), None) == tsg.OK
+    want = -(-(-(-7 // cs) * 6) // 6)
+    assert (P.value, it.value) == (6 * cs, want)
+    assert p.trace_rows() == 6 * cs * want
+    q = tsg.Plan(512, 512, 512, "fp16", 128, 128, 64, 2, 2, num_workgroups=5, cluster_size=2)
+    assert lib.tsgemm_launch_info(q._h, ctypes.byref(P), None, None) == tsg.EINVAL
+    assert "clusters" in tsg.last_error()
 
 
 def test_mx_plan_info_and_dtype_mismatch():

@@ -236,6 +236,20 @@ def _plan_for(w, waves=0):
 
 
 @pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_launch_info_matches_device(cfg):
+    """The grid a run uses: one workgroup per compute unit by default, the
+    busiest worker's waves, and the device's XCD count (8 on MI355X)."""
+    w = WORKLOADS[cfg]
+    plan = _plan_for(w)
+    g = plan.launch_info()
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    P = w.num_workgroups or cus
+    assert g["num_workgroups"] == P == plan.num_workgroups
+    assert g["max_iters"] == _waves(plan, P)
+    assert g["num_xcds"] == 8
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
 def test_schedule_dump_bit_exact(cfg):
     w = WORKLOADS[cfg]
     plan = _plan_for(w)
