@@ -207,6 +207,24 @@ int tsgemm_mx_pack_scales(const tsgemm_plan* plan, int operand, const void* SF, 
 int tsgemm_run_mx_packed(const tsgemm_plan* plan, const void* A, const void* SFAP, const void* B,
                          const void* SFBP, void* C, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * product of tsgemm_run_mx, computed as tsgemm_mx_pack_scales of SFA and of
+ * SFB followed by tsgemm_run_mx_packed, with the packed scales kept in a
+ * static workspace inside the library instead of caller buffers.  Same
+ * arguments and result as tsgemm_run_mx (C bit for bit that of the packed
+ * path).  Allocates nothing (no hipMalloc, no host allocation); the first call
+ * on a device looks up the workspace's device address.
+ *   Limit: packed SFA (rounded up to 256 bytes) + packed SFB at most 16 MiB,
+ *   i.e. about (M + N) * K / 32 <= 16 MiB (8192^3: 4 MiB); larger plans get
+ *   TSGEMM_EUNSUPPORTED before anything is launched.
+ *   The workspace is one per device, held until the process ends, shared by
+ *   every call on that device and left holding the last call's packed
+ *   scales: calls that overlap on one device (different streams or threads
+ *   without ordering between them) race on it. */
+int tsgemm_run_mx_noalloc(const tsgemm_plan* plan, const void* A, const void* SFA, const void* B,
+                          const void* SFB, void* C, void* stream);
+
 /* m_blocks * n_blocks, the tile count the scheduler walks (page "[Feature]
  * Introduce tile scheduler #2441", Files changed: the waves formula
  * ceildiv(m_blocks * n_blocks, sm_num)); < 0 on error. */

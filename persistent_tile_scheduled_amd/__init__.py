@@ -34,7 +34,7 @@ EXPORTS = (
     "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_mx_packed_scale_bytes",
     "tsgemm_mx_pack_scales", "tsgemm_run_mx_packed", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
-    "tsgemm_last_error_code", "tsgemm_launch_info",
+    "tsgemm_last_error_code", "tsgemm_launch_info", "tsgemm_run_mx_noalloc",
 )
 
 
@@ -104,6 +104,8 @@ def load(path: str | None = None):
     lib.tsgemm_mx_pack_scales.restype = i32
     lib.tsgemm_run_mx_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.tsgemm_run_mx_packed.restype = i32
+    lib.tsgemm_run_mx_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.tsgemm_run_mx_noalloc.restype = i32
     lib.tsgemm_num_tiles.argtypes = [vp]
     lib.tsgemm_num_tiles.restype = i64
     lib.tsgemm_num_workgroups.argtypes = [vp]
@@ -268,6 +270,14 @@ class Plan:
         a, sa, b, sb, c = self._mx_args(A, SFA, B, SFB, C)
         s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
         _check(self._lib.tsgemm_run_mx(self._h, a, sa, b, sb, c, s))
+
+    def run_mx_noalloc(self, A, SFA, B, SFB, C, stream=None) -> None:
+        """tsgemm_run_mx_noalloc: run_mx through the packed-scale kernel with the
+        packed scales in the library's static workspace (allocates nothing)."""
+        import torch
+        a, sa, b, sb, c = self._mx_args(A, SFA, B, SFB, C)
+        s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        _check(self._lib.tsgemm_run_mx_noalloc(self._h, a, sa, b, sb, c, s))
 
     def mx_packed_scale_bytes(self, operand: int) -> int:
         """Bytes of the packed scale array of operand 0 (SFA) or 1 (SFB)."""

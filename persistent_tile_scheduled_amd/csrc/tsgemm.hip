@@ -483,6 +483,36 @@ int tsgemm_run_mx_packed(const tsgemm_plan* p, const void* A, const void* SFAP, 
     return run_mx_impl(p, A, SFAP, B, SFBP, C, stream, nullptr, true);
 }
 
+int tsgemm_run_mx_noalloc(const tsgemm_plan* p, const void* A, const void* SFA, const void* B, const void* SFB,
+                          void* C, void* stream) {
+    reset_error();
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (!is_mx(p)) return fail(TSGEMM_EINVAL, "tsgemm_run_mx_noalloc needs a TSGEMM_MXFP8 plan (dtype %d)", p->dtype);
+    if (p->M == 0 || p->N == 0) return TSGEMM_OK;
+    // packed SFA at the workspace start, packed SFB at the next 256-byte boundary
+    const int64_t a_bytes = mx_packed_bytes(p, p->m_blocks), b_bytes = mx_packed_bytes(p, p->n_blocks);
+    const int64_t b_off = (a_bytes + 255) / 256 * 256;
+    if (b_off + b_bytes > tsg::kMxScratchBytes)
+        return fail(TSGEMM_EUNSUPPORTED,
+                    "the packed scales need %lld bytes; the static workspace of tsgemm_run_mx_noalloc holds %lld",
+                    (long long)(b_off + b_bytes), (long long)tsg::kMxScratchBytes);
+    if (p->k_blocks == 0) return run_mx_impl(p, A, SFA, B, SFB, C, stream, nullptr, false);  // C = 0, no scales
+    if (!A || !B || !C || !SFA || !SFB) return fail(TSGEMM_EINVAL, "A, SFA, B, SFB or C is NULL");
+    if ((reinterpret_cast<uintptr_t>(SFA) | reinterpret_cast<uintptr_t>(SFB)) & 3u)
+        return fail(TSGEMM_EINVAL, "SFA and SFB must be 4-byte aligned");
+    void* ws = nullptr;
+    hipError_t e = tsg::mx_scratch_address(&ws);
+    if (e != hipSuccess) return fail(TSGEMM_EHIP, "workspace address: %s", hipGetErrorString(e));
+    uint8_t* sfap = static_cast<uint8_t*>(ws);
+    uint8_t* sfbp = sfap + b_off;
+    // the pack kernels write every byte of both packed arrays (zeros past the
+    // data), so nothing a previous call left in the workspace is read
+    int rc = tsgemm_mx_pack_scales(p, 0, SFA, sfap, stream);
+    if (rc == TSGEMM_OK) rc = tsgemm_mx_pack_scales(p, 1, SFB, sfbp, stream);
+    if (rc != TSGEMM_OK) return rc;
+    return run_mx_impl(p, A, sfap, B, sfbp, C, stream, nullptr, true);
+}
+
 int64_t tsgemm_num_tiles(const tsgemm_plan* p) {
     reset_error();
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");

@@ -42,6 +42,13 @@ TSG_DECLARE_GEMM_TU(2, 256, 32)
 TSG_DECLARE_GEMM_TU(2, 256, 64)
 
 // Block-scaled FP8 kernels (tsgemm_mx_tu.hip).
+// Workspace of the allocation-free MX entry point: packed SFA then packed SFB
+// in one static device array of this many bytes (per device, held until the
+// process ends).
+constexpr int64_t kMxScratchBytes = int64_t(16) << 20;
+// Device address of that array on the current device (looked up once per
+// device); hipSuccess or the lookup's error.
+hipError_t mx_scratch_address(void** ptr);
 void launch_mx(const MxArgs& a, unsigned grid, bool packed, hipStream_t s);
 void launch_mx_pack(const uint8_t* SF, uint8_t* SFP, int64_t rows, uint32_t kb_bytes, uint32_t blocks,
                     uint32_t n_groups, unsigned grid, hipStream_t s);

@@ -1,9 +1,38 @@
 // The block-scaled FP8 (MX) kernels: the GEMM (row-major or packed scales)
 // and the scale-packing permutation.
+#include <mutex>
+
 #include "tsgemm_launch.h"
 #include "tsgemm_mx_kernel.h"
 
 namespace tsg {
+
+// Packed-scale workspace of tsgemm_run_mx_noalloc (see kMxScratchBytes).  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// every host use goes through the address hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) uint8_t scratch[kMxScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device ordinal
+}  // namespace
+
+hipError_t mx_scratch_address(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // Scale packing for the PACKED kernel: SF[rows][K/32] (row-major E8M0) ->
 // SFP[block][group][256][SC_ROW], block = 256-row block, group = SG consecutive
