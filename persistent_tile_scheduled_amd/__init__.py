@@ -67,11 +67,13 @@ _lib = None
 
 
 def load(path: str | None = None):
-    """Load libtsgemm.so (built by __graft_entry__.build()); raises if absent."""
+    """Load libtsgemm.so (built by __graft_entry__.build()); raises if absent.
+    The environment variable TSGEMM_LIB names another build of the library
+    (for instance one compiled with different -D switches) to load instead."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("TSGEMM_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
                            "(persistent_tile_scheduled_amd._build.build_library())")

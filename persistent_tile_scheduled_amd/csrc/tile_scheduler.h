@@ -4,8 +4,10 @@
 // examples/gemm_sm100/gemm_tcgen5mma_ws_persistent.py): each warp role builds
 // its own PersistentTileScheduler, calls init(block_id), loops while valid()
 // and advances with next_tile(); the scheduler's current_iter is the wave index
-// w (pipeline phase, w & 1 double buffering) and m_idx / n_idx are the tile
-// coordinates.  The removed manual walk it replaces gives worker `wid` the
+// w and m_idx / n_idx are the tile coordinates.  (The page selects one of two
+// TMEM accumulators by w & 1; the kernels here keep one accumulator set per
+// wave, and `iter` is exported through the schedule dump and the kernel's
+// trace.)  The removed manual walk it replaces gives worker `wid` the
 // linear tiles P*w + wid and decodes them in groups of group_size column
 // blocks, rows of the group walked one after the other.  The conversation tab
 // describes a stateless coord(tile_id) next to the stateful iteration.
@@ -81,7 +83,6 @@ struct TileScheduler {
         tile_id += num_workers;
         update();
     }
-    TSG_HD uint32_t parity() const { return iter & 1u; }
 
   private:
     // The workgroup takes row block m * cluster + rank of its cluster's tile;

@@ -25,9 +25,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 enum { DT_FP16 = 1, DT_BF16 = 2 };
 #ifndef TSG_DMA_SPACING
-#define TSG_DMA_SPACING 3
+#define TSG_DMA_SPACING 0  // 0: 4 MFMAs for 64-deep slabs, 3 for 32-deep (measured best on MI355X)
 #endif
-constexpr int kDmaSpacing = TSG_DMA_SPACING;  // MFMAs between consecutive DMA issues
+// MFMAs between consecutive DMA issues of a wave, for block_K = bk
+constexpr int dma_spacing(int bk) { return TSG_DMA_SPACING > 0 ? TSG_DMA_SPACING : (bk == 64 ? 4 : 3); }
 #ifndef TSG_DMA_FIRST
 #define TSG_DMA_FIRST 14  // DMAs per slab issued in its first k-step of issue (0: all)
 #endif

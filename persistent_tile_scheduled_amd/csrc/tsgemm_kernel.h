@@ -392,7 +392,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int D0 = LAST ? 0 : T::DF;
         // DMA issues are spaced DS MFMAs apart: a burst of them right after the
         // barrier would overflow the texture unit's queue and stall issue
-        constexpr int DS = D ? (AVAIL / D < kDmaSpacing ? (AVAIL / D > 0 ? AVAIL / D : 1) : kDmaSpacing) : 1;
+        constexpr int DS = D ? (AVAIL / D < dma_spacing(BK) ? (AVAIL / D > 0 ? AVAIL / D : 1) : dma_spacing(BK)) : 1;
         constexpr int QR = SAME ? 0 : R;                   // reads, spread evenly
         constexpr int PER = QR ? (QR + AVAIL - 1) / AVAIL : 0;
         // The loader's step, in the k-step that issues a slab's last DMAs: in
