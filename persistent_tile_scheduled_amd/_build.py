@@ -40,6 +40,15 @@ def _jobs() -> int:
     return max(1, min(n, cap, len(UNITS)))
 
 
+STRESS_OUT = os.path.join(HERE, "libtsgemm_stress.so")
+
+
+def build_stress_library(out: str = STRESS_OUT) -> str:
+    """The race-detection build (-DTSG_STRESS=1: random pauses at every barrier
+    and DMA).  Tests run against it with TSGEMM_LIB=<this file>."""
+    return build_library(out=out, extra_flags=["-DTSG_STRESS=1"])
+
+
 def build_library(out: str = OUT, verbose: bool = False, extra_flags=()) -> str:
     """Compile every unit (in parallel) and link libtsgemm.so at `out`.
     `extra_flags` are added to every compile (e.g. -D switches of a variant build)."""
@@ -69,3 +78,8 @@ def build_library(out: str = OUT, verbose: bool = False, extra_flags=()) -> str:
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     return out
+
+
+if __name__ == "__main__":
+    import sys
+    print(build_stress_library() if "--stress" in sys.argv[1:] else build_library())

@@ -43,10 +43,46 @@ constexpr int dma_spacing(int bk) { return TSG_DMA_SPACING > 0 ? TSG_DMA_SPACING
 #endif
 constexpr int kGap = TSG_GAP;  // MFMAs between the last read of a fragment set and its refill
 
-// Idle issue slots covering an in-flight MFMA's operand fetch and result write
-// (MFMAs here are asm, so the compiler inserts no wait states for them).
-__device__ __forceinline__ void gap_nops() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-__device__ __forceinline__ void store_gap() { asm volatile("s_nop 7\n\ts_nop 7" ::: "memory"); }
+#ifndef TSG_STRESS
+#define TSG_STRESS 0  // 1: race-detection build, pauses at every synchronisation site (tests only)
+#endif
+
+// Race-detection build: a pseudo-random pause of 0 to ~2048 cycles, different
+// for every wave, site and call, before and after each workgroup barrier and
+// before each LDS-DMA.  Shifting the waves against each other this way makes a
+// missing wait (a stage refilled while another wave still reads it, or read
+// before its data landed) show up as wrong results.  s_sleep always ends, so a
+// pause never hangs a wave.  Compiles to nothing in the normal build.
+template <int SITE>
+__device__ __forceinline__ void stress_pause(uint32_t wave, uint32_t& ctr) {
+    if constexpr (TSG_STRESS != 0) {
+        ++ctr;
+        const uint32_t h = ((wave + 1u) * 0x9E3779B1u) ^ (ctr * 0x85EBCA77u) ^ ((uint32_t)(SITE + 1) * 0xC2B2AE3Du);
+        switch ((h ^ (h >> 15)) & 7u) {
+            case 3: __builtin_amdgcn_s_sleep(1); break;
+            case 4: __builtin_amdgcn_s_sleep(4); break;
+            case 5: __builtin_amdgcn_s_sleep(8); break;
+            case 6: __builtin_amdgcn_s_sleep(16); break;
+            case 7: __builtin_amdgcn_s_sleep(32); break;
+            default: break;
+        }
+    } else {
+        (void)wave;
+        (void)ctr;
+    }
+}
+
+// Wait states the compiler cannot place itself, because the instructions
+// involved sit inside inline asm (its hazard recognizer does not look into an
+// asm block for these pairs).  The counts are the ones gfx950 code generation
+// inserts for the same pairs written with compiler-visible instructions:
+//   gap_nops:  a 16x16x32 MFMA's result -> a VALU read of it (here the
+//              v_accvgpr_read of the conversion): 8 wait states (s_nop 7);
+//   store_gap: a 16-byte buffer store -> a write of its data registers: 2
+//              (s_nop 1; the compiler adds the same two itself when the
+//              writer is an asm block, so this is a second guard).
+__device__ __forceinline__ void gap_nops() { asm volatile("s_nop 7" ::: "memory"); }
+__device__ __forceinline__ void store_gap() { asm volatile("s_nop 1" ::: "memory"); }
 constexpr uint32_t kRawBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
 
 struct GemmArgs {

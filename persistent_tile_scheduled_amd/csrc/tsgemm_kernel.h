@@ -87,6 +87,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K;
     const uint32_t k_blocks = args.k_blocks;
     const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
+    uint32_t stress_ctr = 0;  // race-detection build only (TSG_STRESS)
 
     // ---- DMA source offsets (bytes from the slab origin) = lane part + uniform part ----
     // Instruction q of this wave fills 16-byte LDS positions p = qe*64 + lane,
@@ -237,6 +238,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     };
     auto load_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int q = decltype(q_c)::value;
+        stress_pause<2>(wave, stress_ctr);
         const uint32_t v = voff[q];
         if constexpr (q < NA)
             dma16_m0(v, rs_a);
@@ -323,8 +325,8 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // A worker's first tile stores nothing in its first k-step (an empty
     // store window); its last tile stores the remaining blocks after the
     // loop.  Stores are two MFMAs apart, so a store's data registers stay
-    // intact for 32+ cycles before the next conversion (what store_gap gives
-    // the plain epilogue).
+    // intact for 32+ cycles before the next conversion overwrites them (two
+    // wait states are required, store_gap).
     constexpr bool kEpiInterleave = TSG_EPI_INTERLEAVE && KS == 2 && EPI == 0 && WGN == 2 && FM % 2 == 0 && FN % 2 == 0;
     // MFMAs issued between a block's last MFMA and the first read of its
     // accumulators: the MFMAs are asm the compiler cannot see, so the wait
@@ -411,8 +413,10 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             else
                 mfma16x16x32<DT>(acc[fm][fn], bv, fa[CUR][fm]);
             if constexpr (LAST && s == S0 - 1) {
+                stress_pause<0>(wave, stress_ctr);
                 wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
                 lds_barrier();                                       // ... for every wave; stage phase free
+                stress_pause<1>(wave, stress_ctr);
             }
             if constexpr (s + 1 >= START) {
                 // addresses of the reads issued in the next step
@@ -508,6 +512,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                         });
                     });
                 }
+                stress_pause<4>(wave, stress_ctr);
                 lds_barrier();  // the chunk is complete in LDS
                 static_for<0, ROUNDS>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
@@ -520,6 +525,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                     __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? (r * N + col) * 2u : 0x80000000u, 0, 0);
                     store_gap();
                 });
+                stress_pause<5>(wave, stress_ctr);
                 lds_barrier();  // every read of the chunk done before it is rewritten
             });
             // the k == 0 clear, once for the whole tile: clearing inside the
@@ -561,9 +567,8 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                 const bool ok = row_ok && col0 + 32u * t < cols_left;
                 __builtin_amdgcn_raw_buffer_store_b128(v, rc, (ok ? lane_off : 0x80000000u) + t * 64,
                                                        fm * 16 * N * 2, 0);
-                // The store may read its data registers after it issues (a second
-                // wave's memory traffic can hold it back); keep them intact for a
-                // while before the next conversion overwrites them.
+                // the store's data registers are read after it issues: two wait
+                // states before the next conversion overwrites them
                 store_gap();
                 acc[fm][2 * t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 acc[fm][2 * t + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -584,6 +589,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             if constexpr (!kSplitAdvance) slab_advance();
         }
     }
+    stress_pause<3>(wave, stress_ctr);
     wait_vm<(L - 2) * NL + T::DF < 63 ? (L - 2) * NL + T::DF : 63>();
     lds_barrier();
     read_all(I0{}, I0{}, 0u);

@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t stress_ctr = 0;  // race-detection build only (TSG_STRESS)
     const uint32_t wr = wave >> 1, wc = wave & 1u;
     const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K, KB = K / 32u;
     const uint32_t k_blocks = args.k_blocks;
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     auto dma_op = [&](auto q_c) __attribute__((always_inline)) {
         constexpr int qq = decltype(q_c)::value;
         constexpr int q = qq < T::DF ? qq + NSC : (qq < T::DF + NSC ? qq - T::DF : qq);
+        stress_pause<2>(wave, stress_ctr);
         if constexpr (q < NSC) {
             constexpr int i = q % NS;
             if (sc_issue)
@@ -470,8 +472,10 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
             if constexpr (LAST && s == 0) slab_desc();
             if constexpr (LAST && s == ADV) slab_advance();
             if constexpr (LAST && s == S0 - 1) {
+                stress_pause<0>(wave, stress_ctr);
                 wait_vm<0>();    // slab phase+1 (and its scale group) has landed
                 lds_barrier();   // ... for every wave; stage phase and scale entries read are free
+                stress_pause<1>(wave, stress_ctr);
                 set_addr(ksn_c, read_st, read_scb);
             }
             if constexpr (s >= START) {
@@ -515,6 +519,7 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         else  // the last prologue slab's chunks [DF, ND) follow in the first k-step
             static_for<0, T::DF + NSC>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
     }
+    stress_pause<3>(wave, stress_ctr);
     wait_vm<0>();
     lds_barrier();
     auto scale_base = [&](uint32_t grp, uint32_t sub) __attribute__((always_inline)) -> uint32_t {

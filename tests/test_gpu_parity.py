@@ -329,14 +329,26 @@ def test_full_size_every_element(cfg, waves):
           f"worst row {row:.3g}, worst column {col:.3g}", flush=True)
 
 
-def test_deterministic_repeat():
-    """Each tile is owned by one workgroup with a fixed order: runs are bit-identical."""
-    w = WORKLOADS["cfg2_1024_fp16"]
-    A, B = workload_inputs(w)
-    plan = _plan_for(w)
-    C1, _ = _run(plan, A, B, w.dtype)
-    C2, _ = _run(plan, A, B, w.dtype)
-    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("cfg", ["cfg2_1024_fp16", "cfg3_8192_bf16", "cfg4p_16000x4000x4096_fp16"])
+def test_deterministic_repeat(cfg, waves):
+    """Each tile is owned by one workgroup and sums its slabs in a fixed order,
+    so repeated runs give C bit for bit; a race on a stage (a slab refilled
+    while a wave still reads it, or read before it landed) would not."""
+    w = WORKLOADS[cfg]
+    print(f"[case] determinism {cfg} waves={waves}", flush=True)
+    A, B = (_FULL_REF[cfg][:2] if cfg in _FULL_REF else workload_inputs(w))
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    plan = _plan_for(w, waves)
+    outs = []
+    for rep in range(3):
+        C = torch.full((w.M, w.N), float("nan"), dtype=TDT[w.dtype], device=DEV)
+        plan.run(Ad, Bd, C)
+        torch.cuda.synchronize()
+        outs.append(C)
+    assert torch.isfinite(outs[0].float()).all()
+    for C in outs[1:]:
+        assert torch.equal(C.view(torch.int16), outs[0].view(torch.int16))
 
 
 # ---------------------------------------------------------------- scheduler options
