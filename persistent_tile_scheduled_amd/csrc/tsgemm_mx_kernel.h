@@ -60,10 +60,13 @@ struct MxArgs {
 
 // acc += src0 x src1 with per-row E8M0 scales (byte 0 of each scale
 // register, op_sel 0), both operands E4M3.  Accumulator constrained to AGPRs
-// as in the fp16/bf16 kernel.  The leading s_nop gives the two wait states an
-// MFMA needs after a VALU write of one of its source VGPRs: the compiler
+// as in the fp16/bf16 kernel.  The leading s_nop 1 covers the wait state an
+// MFMA needs after a VALU write of one of its source or scale VGPRs (gfx950
+// code generation places one, s_nop 0, for that pair): the compiler
 // zero-extends the scale bytes with VALU ops it may place right before this
-// asm, and it pads only instructions it knows to be MFMAs.
+// asm, and it pads only instructions it knows to be MFMAs.  Reading a result
+// needs 20 wait states after this 64-cycle MFMA; the epilogue reads a block
+// four MFMAs after its last one.
 __device__ __forceinline__ void mfma_mx32(f32x16& acc, i32x8 src0, i32x8 src1, uint32_t s0, uint32_t s1) {
     asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                  : "+a"(acc) : "v"(src0), "v"(src1), "v"(s0), "v"(s1));
