@@ -136,6 +136,16 @@ int tsgemm_set_epilogue(tsgemm_plan* plan, int store_block_N);
  * permutation.  The schedule is defined on worker ids either way. */
 int tsgemm_set_xcd_remap(tsgemm_plan* plan, int enable);
 
+/* The workgroup -> worker id permutation a run uses (host only, no HIP call):
+ * out[b] = worker id of workgroup b, for b < num_workgroups.  Workgroup b runs
+ * on XCD b % num_xcds; each XCD gets contiguous runs of worker ids, and the
+ * first num_active ids (the workers that have tiles: fewer than the
+ * workgroups when the tiles run out) are split evenly over the XCDs.  A
+ * permutation of [0, num_workgroups); TSGEMM_EINVAL unless num_workgroups,
+ * num_xcds > 0 and 0 < num_active <= num_workgroups.  Not on the pages: the
+ * renumbering is this implementation's (XCDs have separate L2 caches). */
+int tsgemm_worker_numbering(int32_t num_workgroups, int32_t num_xcds, int32_t num_active, int32_t* out);
+
 /* Asynchronously compute C = A*B on `stream` (a hipStream_t; NULL = default
  * stream).  The launch of page "tilelang" section 1.3 (call(A, B, C, stream):
  * one kernel on the caller's stream, 0 or an error code back); the product

@@ -34,7 +34,7 @@ EXPORTS = (
     "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_mx_packed_scale_bytes",
     "tsgemm_mx_pack_scales", "tsgemm_run_mx_packed", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
-    "tsgemm_last_error_code", "tsgemm_launch_info", "tsgemm_run_mx_noalloc",
+    "tsgemm_last_error_code", "tsgemm_launch_info", "tsgemm_run_mx_noalloc", "tsgemm_worker_numbering",
 )
 
 
@@ -126,6 +126,8 @@ def load(path: str | None = None):
     lib.tsgemm_last_error_code.restype = i32
     lib.tsgemm_launch_info.argtypes = [vp, i32p, i32p, i32p]
     lib.tsgemm_launch_info.restype = i32
+    lib.tsgemm_worker_numbering.argtypes = [i32, i32, i32, i32p]
+    lib.tsgemm_worker_numbering.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -323,6 +325,14 @@ class Plan:
         t = self._check_trace(trace)
         s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
         _check(self._lib.tsgemm_run_mx_traced(self._h, a, sa, b, sb, c, s, t))
+
+
+def worker_numbering(num_workgroups: int, num_xcds: int, num_active: int) -> np.ndarray:
+    """tsgemm_worker_numbering: the worker id of every workgroup."""
+    out = np.empty(num_workgroups, dtype=np.int32)
+    _check(load().tsgemm_worker_numbering(num_workgroups, num_xcds, num_active,
+                                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return out
 
 
 def matmul(A, B, block_M=256, block_N=256, block_K=64, group_size=8, num_stages=3):

@@ -104,14 +104,23 @@ struct TileScheduler {
 };
 
 // Hardware hands workgroups to the XCDs round robin (workgroup b runs on XCD
-// b % X).  Renumber them so that XCD x holds a contiguous run of worker ids:
+// b % X).  Renumber them so that each XCD holds contiguous runs of worker ids:
 // consecutive tile ids, hence a compact block of one column group, then share
-// that XCD's L2.  A bijection on [0, P) for every P.
-TSG_HD uint32_t worker_of_workgroup(uint32_t b, uint32_t P, uint32_t X) {
+// that XCD's L2.  Only the first A worker ids have tiles when the tile count
+// is below the worker count, so those are split evenly over the XCDs (XCD x
+// gets active ids [x*qa + min(x, ra), ...) with qa = A / X, ra = A % X) and the
+// idle ids fill the remaining slots; with A = P every XCD simply gets one run.
+// A bijection on [0, P) for every P, X >= 1 and 1 <= A <= P.
+TSG_HD uint32_t worker_of_workgroup(uint32_t b, uint32_t P, uint32_t X, uint32_t A) {
     if (X <= 1u) return b;
     const uint32_t x = b % X, j = b / X;
-    const uint32_t q = P / X, r = P % X;
-    return x * q + (x < r ? x : r) + j;
+    const uint32_t q = P / X, r = P % X;      // XCD x holds q + (x < r) workgroups
+    const uint32_t qa = A / X, ra = A % X;    // ... of which qa + (x < ra) are active
+    const uint32_t active_x = qa + (x < ra ? 1u : 0u);
+    const uint32_t first_active = x * qa + (x < ra ? x : ra);
+    if (j < active_x) return first_active + j;
+    const uint32_t first_slot = x * q + (x < r ? x : r);
+    return A + (first_slot - first_active) + (j - active_x);
 }
 
 }  // namespace tsg

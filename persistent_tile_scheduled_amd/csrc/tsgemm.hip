@@ -31,9 +31,9 @@ __global__ void tsgemm_zero_kernel(uint16_t* C, int64_t count8) {
 // Schedule dump: the same scheduler and worker numbering as the GEMM kernel.
 __global__ void tsgemm_schedule_kernel(uint32_t P, uint32_t m_blocks, uint32_t n_blocks,
                                        uint32_t group, uint32_t cluster, uint32_t col_major,
-                                       uint32_t num_xcd, uint32_t max_iters, int32_t* out) {
+                                       uint32_t num_xcd, uint32_t num_active, uint32_t max_iters, int32_t* out) {
     if (threadIdx.x != 0) return;
-    const uint32_t wid = worker_of_workgroup(blockIdx.x, P, num_xcd);
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, P, num_xcd, num_active);
     TileScheduler s;
     s.setup(P, m_blocks, n_blocks, group, cluster, col_major);
     for (s.init(wid); s.valid(); s.next_tile()) {
@@ -172,6 +172,7 @@ namespace {
 
 struct Grid {
     uint32_t P, xcds, max_iters;
+    uint32_t active;  // workers with at least one tile: whole clusters, at most P
 };
 
 bool is_mx(const tsgemm_plan* p) { return p->dtype == TSGEMM_MXFP8; }
@@ -201,6 +202,10 @@ int resolve_grid(const tsgemm_plan* p, Grid* g) {
     if (g->P % (uint32_t)p->cluster != 0)
         return fail(TSGEMM_EINVAL, "the %u workgroups do not split into clusters of %d", g->P, p->cluster);
     g->max_iters = max_iters_for(p, g->P);
+    const int64_t clusters = g->P / (uint32_t)p->cluster;
+    const int64_t cluster_tiles = (p->m_blocks + p->cluster - 1) / p->cluster * p->n_blocks;
+    g->active = (uint32_t)((cluster_tiles < clusters ? cluster_tiles : clusters) * p->cluster);
+    if (g->active == 0) g->active = g->P;  // no tiles: nothing to spread
     return TSGEMM_OK;
 }
 
@@ -231,6 +236,7 @@ int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* 
     a.P = g.P;
     a.max_iters = g.max_iters;
     a.num_xcd = g.xcds;
+    a.num_active = g.active;
     a.cluster = (uint32_t)p->cluster;
     a.col_major = (uint32_t)p->col_major;
     (void)hipGetLastError();
@@ -297,6 +303,7 @@ int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void
         a.P = g.P;
         a.max_iters = g.max_iters;
         a.num_xcd = g.xcds;
+    a.num_active = g.active;
         a.cluster = (uint32_t)p->cluster;
         a.col_major = (uint32_t)p->col_major;
         a.n_groups = mx_groups(p);
@@ -592,6 +599,17 @@ int tsgemm_schedule_host(const tsgemm_plan* p, int num_workgroups, int32_t* out)
     return TSGEMM_OK;
 }
 
+int tsgemm_worker_numbering(int32_t num_workgroups, int32_t num_xcds, int32_t num_active, int32_t* out) {
+    reset_error();
+    if (!out) return fail(TSGEMM_EINVAL, "out is NULL");
+    if (num_workgroups <= 0 || num_xcds <= 0 || num_active <= 0 || num_active > num_workgroups)
+        return fail(TSGEMM_EINVAL, "need num_workgroups > 0, num_xcds > 0 and 0 < num_active <= num_workgroups");
+    for (int32_t b = 0; b < num_workgroups; ++b)
+        out[b] = (int32_t)tsg::worker_of_workgroup((uint32_t)b, (uint32_t)num_workgroups, (uint32_t)num_xcds,
+                                                   (uint32_t)num_active);
+    return TSGEMM_OK;
+}
+
 int tsgemm_dump_schedule(const tsgemm_plan* p, int32_t* out) {
     reset_error();
     if (!p || !out) return fail(TSGEMM_EINVAL, "plan or out is NULL");
@@ -608,7 +626,7 @@ int tsgemm_dump_schedule(const tsgemm_plan* p, int32_t* out) {
     if (e == hipSuccess) {
         hipLaunchKernelGGL(tsg::tsgemm_schedule_kernel, dim3(g.P), dim3(64), 0, 0, g.P, (uint32_t)p->m_blocks,
                            (uint32_t)p->n_blocks, (uint32_t)p->group, (uint32_t)p->cluster,
-                           (uint32_t)p->col_major, g.xcds, g.max_iters, d);
+                           (uint32_t)p->col_major, g.xcds, g.active, g.max_iters, d);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipMemcpy(h.data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost);

@@ -93,6 +93,7 @@ struct GemmArgs {
     int64_t M, N, K;
     uint32_t m_blocks, n_blocks, k_blocks, group;
     uint32_t P, max_iters, num_xcd;
+    uint32_t num_active;          // workers with at least one tile (worker numbering)
     uint32_t cluster, col_major;  // tile scheduler options
 };
 

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     const uint32_t wr = wave / WGN, wc = wave % WGN;  // wave row / column in the 2 x WGN grid
     const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K;
     const uint32_t k_blocks = args.k_blocks;
-    const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd, args.num_active);
     uint32_t stress_ctr = 0;  // race-detection build only (TSG_STRESS)
 
     // ---- DMA source offsets (bytes from the slab origin) = lane part + uniform part ----

@@ -54,6 +54,7 @@ struct MxArgs {
     int64_t M, N, K;
     uint32_t m_blocks, n_blocks, k_blocks, group;
     uint32_t P, max_iters, num_xcd;
+    uint32_t num_active;  // workers with at least one tile (worker numbering)
     uint32_t cluster, col_major;
     uint32_t n_groups;   // scale groups per tile: ceil(k_blocks / SG)
 };
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
     const uint32_t wr = wave >> 1, wc = wave & 1u;
     const uint32_t N = (uint32_t)args.N, K = (uint32_t)args.K, KB = K / 32u;
     const uint32_t k_blocks = args.k_blocks;
-    const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd);
+    const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd, args.num_active);
 
     // ---- DMA source offsets (bytes from the slab origin) ----
     // Instruction q of this wave fills 16-byte LDS positions p = (wave*NA + q)*64

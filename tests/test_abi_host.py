@@ -245,3 +245,29 @@ def test_host_schedule_options_match_oracle(cs, cm):
         plan = tsg.Plan(mb * 128, nb * 128, 64, "bf16", 128, 128, 64, gs, 2, column_major=cm, cluster_size=cs)
         want = np.array(oracle.schedule.schedule(P, mb, nb, gs, column_major=cm, cluster_size=cs), dtype=np.int32)
         assert np.array_equal(plan.schedule_host(P), want), (mb, nb, gs, P, cs, cm)
+
+
+@pytest.mark.parametrize("P,X", [(256, 8), (255, 8), (8, 8), (3, 8), (300, 8), (64, 1), (97, 4)])
+def test_worker_numbering_is_a_balanced_permutation(P, X):
+    """Workgroup b runs on XCD b % X.  The numbering must be a permutation of
+    the worker ids; every XCD must hold contiguous runs of them; and the first
+    A ids (the workers that have tiles) must be split over the XCDs as evenly
+    as possible, so a problem with fewer tiles than workgroups still uses
+    every XCD's L2."""
+    for A in sorted({1, 2, X - 1 if X > 1 else 1, X, X + 3, P // 3, P // 2, P - 1, P}):
+        if not 1 <= A <= P:
+            continue
+        w = tsg.worker_numbering(P, X, A)
+        assert sorted(w.tolist()) == list(range(P)), (P, X, A)
+        if X == 1:
+            assert w.tolist() == list(range(P))
+            continue
+        per_xcd = [w[x::X] for x in range(X)]
+        counts = [int((ids < A).sum()) for ids in per_xcd]
+        assert max(counts) - min(counts) <= 1 and sum(counts) == A, (P, X, A, counts)
+        for ids in per_xcd:
+            act, idle = ids[ids < A], ids[ids >= A]
+            assert np.all(np.diff(act) == 1) and np.all(np.diff(idle) == 1)   # contiguous runs
+            assert np.all(ids[:len(act)] < A)                                 # active slots first
+    with pytest.raises(tsg.TsgemmError):
+        tsg.worker_numbering(P, X, 0)
