@@ -93,7 +93,10 @@ typedef struct tsgemm_info {
  *                MXFP8: 256x256x128 only (K % 128 == 0, two LDS stages).
  *   group_size   >= 1, column blocks per rasterisation group.
  *   num_stages   >= 2: K-slabs in flight; the LDS ring holds
- *                min(num_stages, floor(160 KiB / stage_bytes)) of them.
+ *                min(num_stages, floor(160 KiB / stage_bytes), 5) of them.  A
+ *                request deeper than that is not an error: the plan runs with
+ *                the ring that fits and reports it as tsgemm_info.lds_slots
+ *                (e.g. 256x256x64 tiles, 64 KiB a stage: 3 requested, 2 held).
  * The number of workgroups defaults to one per compute unit of the device
  * current at the first run (see tsgemm_set_num_workgroups).
  */
