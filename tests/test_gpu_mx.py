@@ -271,6 +271,8 @@ def test_mx_full_size_every_element(name, packed):
     d2, r2 = (got - cref) ** 2, cref ** 2
     row = np.sqrt(d2.sum(axis=1) / r2.sum(axis=1)).max()
     col = np.sqrt(d2.sum(axis=0) / r2.sum(axis=0)).max()
+    # per row and column (2e-3): one wrong block scale moves its whole row of C by ~6%
+    assert row <= 2e-3 and col <= 2e-3, f"worst row {row}, worst column {col}"
     print(f"  max err/bound {(err / bound).max():.3g}, max err/mag {(err / mag).max():.3g}, "
           f"rel. Frobenius vs rounded oracle {fro:.3g} (vs exact {np.linalg.norm(got - c64) / np.linalg.norm(c64):.3g}), "
           f"worst row {row:.3g}, worst column {col:.3g}", flush=True)

@@ -327,6 +327,9 @@ def test_full_size_every_element(cfg, waves):
     row, col = _row_col_fro(got, ref)
     print(f"  max |err| {err_max:.3g}, worst err/bound {worst:.3g}, rel. Frobenius {fro:.3g}, "
           f"worst row {row:.3g}, worst column {col:.3g}", flush=True)
+    # the Frobenius criterion row by row and column by column (2e-3: a row's error against the
+    # once-rounded oracle is only its rare one-ulp flips; a localized fault moves a row by %)
+    assert row <= 2e-3 and col <= 2e-3, f"worst row {row}, worst column {col}"
 
 
 @pytest.mark.parametrize("waves", [4, 8])
