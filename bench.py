@@ -22,7 +22,10 @@ plus tsgemm_run_mx_packed, or with --mx-scales rowmajor tsgemm_run_mx alone;
 roofline: the GEMM kernel against the dense fp8 MFMA peak; cpu_baseline the MX
 oracle; context torch's per-tensor-scaled fp8 product when available).  --cold
 rewrites a 512 MiB buffer before every timed launch so the small shapes are not
-served from the Infinity Cache.
+served from the Infinity Cache.  --power S (off by default; after the timed
+steps, so the timed region is the same) runs the step back to back for S seconds
+while `amd-smi metric` samples the board's socket power and graphics clocks, and
+does the same for torch's A @ B; it reports watts, clocks and joules per step.
 """
 
 from __future__ import annotations
@@ -30,7 +33,10 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -168,6 +174,56 @@ def torch_context(torch, Ad, Bd, w, stream, warmup, steps):
     return {"torch_matmul_ms": round(ms, 4), "torch_matmul_tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
 
 
+def _smi_sample():
+    """One `amd-smi metric -p -c` reading: (socket watts, [GFX clock MHz per XCD]) or None."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=15)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+    clks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)]
+    return (float(m.group(1)), clks) if m else None
+
+
+def measure_power(torch, enqueue, seconds: float, settle: float = 1.5):
+    """Run `enqueue` (which queues a few launches) back to back for `seconds`
+    and sample board power from a side thread once the load has run `settle`
+    seconds.  Returns watts, clocks, launches and the mean time per launch."""
+    stop = threading.Event()
+    samples = []
+
+    def sampler():
+        if stop.wait(settle):
+            return
+        while not stop.is_set():
+            s = _smi_sample()
+            if s is None:
+                return
+            samples.append(s)
+            stop.wait(0.25)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        n += enqueue()
+        torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    if not samples:
+        return {"error": "amd-smi gave no socket-power reading"}
+    watts = sum(s[0] for s in samples) / len(samples)
+    clks = [c for s in samples for c in s[1]]
+    ms = dt / n * 1e3
+    return {"samples": len(samples), "socket_w": round(watts, 1),
+            "gfx_mhz_mean": round(sum(clks) / len(clks)) if clks else None,
+            "gfx_mhz_range": [round(min(clks)), round(max(clks))] if clks else None,
+            "launches": n, "ms_per_launch": round(ms, 4), "joules_per_launch": round(watts * ms * 1e-3, 4)}
+
+
 def copy_mode(args, torch):
     """Plain device-to-device copy of a known size: reads and writes
     copy-mib MiB per launch.  Its FETCH_SIZE / WRITE_SIZE counter readings give
@@ -216,6 +272,9 @@ def main():
                     help="also print every timed launch's kernel time, in launch order, to stderr")
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="MX workload: pack the scales on the device each step (default) or feed them row-major")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run the step (and torch's A @ B) back to back this long while "
+                         "amd-smi samples socket power and clocks (0: off)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -354,6 +413,22 @@ def main():
     if not args.no_torch_context:
         out["context"] = (torch_context_fp8 if mx else torch_context)(torch, Ad, Bd, w, stream,
                                                                       args.warmup, args.steps)
+    if args.power > 0:
+        def ours():
+            for _ in range(8):
+                launch()
+            return 8
+        pw = {"kernel": measure_power(torch, ours, args.power)}
+        if not mx:
+            def lib():
+                for _ in range(8):
+                    torch.matmul(Ad, Bd)
+                return 8
+            pw["torch_matmul"] = measure_power(torch, lib, args.power)
+        for v in pw.values():
+            if "joules_per_launch" in v:
+                v["tflops_per_w"] = round(w.flops / v["joules_per_launch"] / 1e12, 3)
+        out["power"] = pw
     if not args.no_cpu_baseline:
         if args.cpu_threads > 0:
             import oracle
