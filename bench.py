@@ -22,10 +22,11 @@ plus tsgemm_run_mx_packed, or with --mx-scales rowmajor tsgemm_run_mx alone;
 roofline: the GEMM kernel against the dense fp8 MFMA peak; cpu_baseline the MX
 oracle; context torch's per-tensor-scaled fp8 product when available).  --cold
 rewrites a 512 MiB buffer before every timed launch so the small shapes are not
-served from the Infinity Cache.  --power S (off by default; after the timed
-steps, so the timed region is the same) runs the step back to back for S seconds
-while `amd-smi metric` samples the board's socket power and graphics clocks, and
-does the same for torch's A @ B; it reports watts, clocks and joules per step.
+served from the Infinity Cache.  --power S (4 s by default, 0 = off; after the
+timed steps, so the timed region is the same) runs the step back to back for S
+seconds while `amd-smi metric` samples the board's socket power and graphics
+clocks, and does the same for torch's A @ B; it reports watts, clocks and
+joules per step ("power").
 """
 
 from __future__ import annotations
@@ -174,15 +175,21 @@ def torch_context(torch, Ad, Bd, w, stream, warmup, steps):
     return {"torch_matmul_ms": round(ms, 4), "torch_matmul_tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
 
 
+def parse_smi(text: str):
+    """(socket watts, [GFX clock MHz per XCD]) from the text of `amd-smi metric -p -c`, or None
+    when it holds no socket-power reading."""
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    return (float(m.group(1)), clks) if m else None
+
+
 def _smi_sample():
-    """One `amd-smi metric -p -c` reading: (socket watts, [GFX clock MHz per XCD]) or None."""
+    """One `amd-smi metric -p -c` reading (see parse_smi), or None."""
     try:
         r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=15)
     except (OSError, subprocess.SubprocessError):
         return None
-    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
-    clks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)]
-    return (float(m.group(1)), clks) if m else None
+    return parse_smi(r.stdout)
 
 
 def measure_power(torch, enqueue, seconds: float, settle: float = 1.5):
@@ -272,7 +279,7 @@ def main():
                     help="also print every timed launch's kernel time, in launch order, to stderr")
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="MX workload: pack the scales on the device each step (default) or feed them row-major")
-    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+    ap.add_argument("--power", type=float, default=4.0, metavar="SECONDS",
                     help="after the timed steps, run the step (and torch's A @ B) back to back this long while "
                          "amd-smi samples socket power and clocks (0: off)")
     args = ap.parse_args()
@@ -419,7 +426,7 @@ def main():
                 launch()
             return 8
         pw = {"kernel": measure_power(torch, ours, args.power)}
-        if not mx:
+        if not mx and not args.no_torch_context:
             def lib():
                 for _ in range(8):
                     torch.matmul(Ad, Bd)
