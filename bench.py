@@ -279,6 +279,8 @@ def main():
                     help="also print every timed launch's kernel time, in launch order, to stderr")
     ap.add_argument("--mx-scales", choices=["packed", "rowmajor"], default="packed",
                     help="MX workload: pack the scales on the device each step (default) or feed them row-major")
+    ap.add_argument("--no-l2-prefetch", action="store_true",
+                    help="workers without a tile leave at once instead of warming their XCD's L2")
     ap.add_argument("--power", type=float, default=4.0, metavar="SECONDS",
                     help="after the timed steps, run the step (and torch's A @ B) back to back this long while "
                          "amd-smi samples socket power and clocks (0: off)")
@@ -311,7 +313,8 @@ def main():
         Ad, Bd = A.to(dev), B.to(dev)
         C = torch.empty((w.M, w.N), dtype=w.torch_dtype, device=dev)
     plan = tsg.Plan(w.M, w.N, w.K, w.dtype, w.block_M, w.block_N, w.block_K, w.group_size,
-                    w.num_stages, num_workgroups=w.num_workgroups, store_block_N=0 if mx else args.epilogue)
+                    w.num_stages, num_workgroups=w.num_workgroups, store_block_N=0 if mx else args.epilogue,
+                    l2_prefetch=False if args.no_l2_prefetch else None)
     info = plan.info()
     P = plan.num_workgroups
     stream = torch.cuda.current_stream(dev)
@@ -395,7 +398,7 @@ def main():
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K,
             "tile": [w.block_M, w.block_N, w.block_K], "group_size": w.group_size,
             "num_stages": w.num_stages, "lds_slots": info["lds_slots"], "num_workgroups": P,
-            "store_block_N": info["store_block_N"],
+            "store_block_N": info["store_block_N"], "l2_prefetch": info["l2_prefetch"],
             "inputs": (f"normal(0,1) MX-encoded (E4M3 + E8M0 per 32 along K), seed {w.seed}" if mx
                        else f"{w.dist}, seed {w.seed}"),
             **({"scales": ("row-major, packed on the device inside every step" if packed else "row-major")}

@@ -73,6 +73,7 @@ typedef struct tsgemm_info {
     int32_t cluster_size;    /* tile scheduler: workgroups per cluster (1 = none)     */
     int32_t column_major;    /* tile scheduler: 1 = transposed tile walk              */
     int32_t store_block_N;   /* epilogue: 0 = direct stores, 64 = staged through LDS  */
+    int32_t l2_prefetch;     /* 1: workers without a tile warm their XCD's L2 (tsgemm_set_l2_prefetch) */
 } tsgemm_info;
 
 /*
@@ -138,6 +139,16 @@ int tsgemm_set_epilogue(tsgemm_plan* plan, int store_block_N);
 /* Enable (1, default) or disable (0) the XCD-aware workgroup -> worker id
  * permutation.  The schedule is defined on worker ids either way. */
 int tsgemm_set_xcd_remap(tsgemm_plan* plan, int enable);
+
+/* With fewer tiles than workgroups, the workers that get no tile (the page's
+ * persistent loop would end for them at once) instead warm the L2 of the XCD
+ * they run on: they load one word of every 128-byte line of the A row panel
+ * and B column panel that the XCD's active workers will stream, in K order,
+ * and leave.  enable = 1 (default for fp16/bf16 plans) or 0 (they leave at
+ * once).  The tile walk and C are the same either way; it shortens launches
+ * whose inputs are not already in the Infinity Cache.  TSGEMM_EINVAL for
+ * enable outside {0, 1}; TSGEMM_EUNSUPPORTED for enable = 1 on an MXFP8 plan. */
+int tsgemm_set_l2_prefetch(tsgemm_plan* plan, int enable);
 
 /* The workgroup -> worker id permutation a run uses (host only, no HIP call):
  * out[b] = worker id of workgroup b, for b < num_workgroups.  Workgroup b runs

@@ -30,7 +30,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM = 0, -1, -2, -3, -4
 # every symbol the header declares
 EXPORTS = (
     "tsgemm_create", "tsgemm_set_num_workgroups", "tsgemm_set_waves", "tsgemm_set_schedule", "tsgemm_set_epilogue",
-    "tsgemm_set_xcd_remap", "tsgemm_run",
+    "tsgemm_set_xcd_remap", "tsgemm_set_l2_prefetch", "tsgemm_run",
     "tsgemm_run_traced", "tsgemm_run_mx", "tsgemm_run_mx_traced", "tsgemm_mx_packed_scale_bytes",
     "tsgemm_mx_pack_scales", "tsgemm_run_mx_packed", "tsgemm_num_tiles", "tsgemm_num_workgroups", "tsgemm_plan_info",
     "tsgemm_dump_schedule", "tsgemm_schedule_host", "tsgemm_destroy", "tsgemm_last_error",
@@ -56,7 +56,7 @@ class Info(ctypes.Structure):
         ("num_workgroups", ctypes.c_int32), ("waves", ctypes.c_int32),
         ("threads_per_workgroup", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
         ("cluster_size", ctypes.c_int32), ("column_major", ctypes.c_int32),
-        ("store_block_N", ctypes.c_int32),
+        ("store_block_N", ctypes.c_int32), ("l2_prefetch", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -92,6 +92,8 @@ def load(path: str | None = None):
     lib.tsgemm_set_epilogue.restype = i32
     lib.tsgemm_set_xcd_remap.argtypes = [vp, i32]
     lib.tsgemm_set_xcd_remap.restype = i32
+    lib.tsgemm_set_l2_prefetch.argtypes = [vp, i32]
+    lib.tsgemm_set_l2_prefetch.restype = i32
     lib.tsgemm_run.argtypes = [vp, vp, vp, vp, vp]
     lib.tsgemm_run.restype = i32
     lib.tsgemm_run_traced.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -151,7 +153,8 @@ class Plan:
 
     def __init__(self, M: int, N: int, K: int, dtype, block_M: int, block_N: int, block_K: int,
                  group_size: int, num_stages: int, num_workgroups: int = 0, xcd_remap: bool = True,
-                 waves: int = 0, column_major: bool = False, cluster_size: int = 1, store_block_N: int = 0):
+                 waves: int = 0, column_major: bool = False, cluster_size: int = 1, store_block_N: int = 0,
+                 l2_prefetch: bool | None = None):
         lib = load()
         self._lib = lib
         dt = _DTYPES.get(dtype)
@@ -172,6 +175,8 @@ class Plan:
             _check(lib.tsgemm_set_schedule(self._h, 1 if column_major else 0, cluster_size))
         if store_block_N:
             _check(lib.tsgemm_set_epilogue(self._h, store_block_N))
+        if l2_prefetch is not None:
+            _check(lib.tsgemm_set_l2_prefetch(self._h, 1 if l2_prefetch else 0))
 
     def __del__(self):
         h = getattr(self, "_h", None)

@@ -165,6 +165,7 @@ struct tsgemm_plan {
     int cluster;   // workgroups per cluster (tile scheduler option), >= 1
     int col_major; // 1 = transposed tile walk (tile scheduler option)
     int epi;       // 0 = direct stores, 64 = C staged through LDS in 64-column chunks
+    int prefetch;  // 1 = workers without a tile warm their XCD's L2 (fp16/bf16 kernels)
     const KernelEntry* kernel;  // fp16/bf16 kernel; NULL for an MXFP8 plan
 };
 
@@ -239,6 +240,7 @@ int run_impl(const tsgemm_plan* p, const void* A, const void* B, void* C, void* 
     a.num_active = g.active;
     a.cluster = (uint32_t)p->cluster;
     a.col_major = (uint32_t)p->col_major;
+    a.prefetch = p->prefetch && g.active < g.P ? 1u : 0u;
     (void)hipGetLastError();
     if (p->k_blocks == 0) {
         // empty sum: C = 0 (N % 8 == 0, so 8 elements per thread)
@@ -303,7 +305,7 @@ int run_mx_impl(const tsgemm_plan* p, const void* A, const void* SFA, const void
         a.P = g.P;
         a.max_iters = g.max_iters;
         a.num_xcd = g.xcds;
-    a.num_active = g.active;
+        a.num_active = g.active;
         a.cluster = (uint32_t)p->cluster;
         a.col_major = (uint32_t)p->col_major;
         a.n_groups = mx_groups(p);
@@ -377,7 +379,7 @@ tsgemm_plan* tsgemm_create(int64_t M, int64_t N, int64_t K, int dtype, int block
     p->dtype = dtype; p->bm = block_M; p->bn = block_N; p->bk = block_K;
     p->group = group_size; p->stages = num_stages; p->slots = slots;
     p->m_blocks = mb; p->n_blocks = nb; p->k_blocks = K / block_K; p->tiles = mb * nb;
-    p->P = 0; p->xcd_remap = 1; p->cluster = 1; p->col_major = 0; p->epi = 0; p->kernel = k;
+    p->P = 0; p->xcd_remap = 1; p->cluster = 1; p->col_major = 0; p->epi = 0; p->prefetch = k ? 1 : 0; p->kernel = k;
     return p;
 }
 
@@ -424,6 +426,15 @@ int tsgemm_set_xcd_remap(tsgemm_plan* p, int enable) {
     if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
     if (enable != 0 && enable != 1) return fail(TSGEMM_EINVAL, "enable must be 0 or 1");
     p->xcd_remap = enable;
+    return TSGEMM_OK;
+}
+
+int tsgemm_set_l2_prefetch(tsgemm_plan* p, int enable) {
+    reset_error();
+    if (!p) return fail(TSGEMM_EINVAL, "plan is NULL");
+    if (enable != 0 && enable != 1) return fail(TSGEMM_EINVAL, "enable must be 0 or 1");
+    if (enable && is_mx(p)) return fail(TSGEMM_EUNSUPPORTED, "the MXFP8 kernel does not warm the L2");
+    p->prefetch = enable;
     return TSGEMM_OK;
 }
 
@@ -575,6 +586,7 @@ int tsgemm_plan_info(const tsgemm_plan* p, tsgemm_info* info) {
     info->cluster_size = p->cluster;
     info->column_major = p->col_major;
     info->store_block_N = p->epi;
+    info->l2_prefetch = p->prefetch;
     return TSGEMM_OK;
 }
 

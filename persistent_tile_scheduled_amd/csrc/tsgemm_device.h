@@ -95,6 +95,7 @@ struct GemmArgs {
     uint32_t P, max_iters, num_xcd;
     uint32_t num_active;          // workers with at least one tile (worker numbering)
     uint32_t cluster, col_major;  // tile scheduler options
+    uint32_t prefetch;            // 1: workers without a tile warm their XCD's L2 (timing only)
 };
 
 // ---------------------------------------------------------------------------

@@ -74,6 +74,72 @@ struct GemmTraits {
 };
 
 
+// With fewer tiles than workers every active worker owns exactly one tile and
+// the others would leave at once.  Instead, each of them warms the L2 of the
+// XCD it runs on (workgroup b runs on XCD b % X) with part of the A row panel
+// and B column panel that one of that XCD's active workers is about to stream:
+// one 4-byte load per 128-byte line, in K order, from the first line the
+// active worker's own prologue does not already request.  The idle workers of
+// an XCD split its active workers round robin and each one's lines among
+// themselves.  Nothing is written; only the timing of the active workers'
+// loads depends on it.
+template <int BM, int BN, int BK, int L>
+__device__ __forceinline__ void warm_l2_for_xcd(const GemmArgs& args) {
+    const uint32_t X = args.num_xcd > 1u ? args.num_xcd : 1u;
+    const uint32_t P = args.P, A = args.num_active;
+    const uint32_t x = blockIdx.x % X, j = blockIdx.x / X;
+    const uint32_t slots = P / X + (x < P % X ? 1u : 0u);
+    const uint32_t active_x = A / X + (x < A % X ? 1u : 0u);
+    const uint32_t first_active = x * (A / X) + (x < A % X ? x : A % X);
+    if (active_x == 0u || j < active_x || j >= slots) return;
+    const uint32_t i = j - active_x, n_idle = slots - active_x;
+    const uint32_t helped = i % active_x;                                 // active worker of this XCD
+    const uint32_t part = i / active_x;                                   // this workgroup's share ...
+    const uint32_t parts = (n_idle - helped + active_x - 1u) / active_x;  // ... of that many
+    TileScheduler s;
+    s.setup(P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
+    s.init(first_active + helped);
+    if (!s.valid()) return;
+    const uint64_t M = (uint64_t)args.M, N = (uint64_t)args.N, K = (uint64_t)args.K;
+    const uint64_t m0 = (uint64_t)s.m_idx * BM, n0 = (uint64_t)s.n_idx * BN;
+    const uint32_t rows_a = (uint32_t)(M - m0 < (uint64_t)BM ? M - m0 : (uint64_t)BM);
+    const uint32_t cols_b = (uint32_t)(N - n0 < (uint64_t)BN ? N - n0 : (uint64_t)BN);
+    const uint32_t row_bytes = (uint32_t)(K * 2u);                      // an A row
+    const uint32_t seg_bytes = cols_b * 2u;                             // a B row's part in the panel
+    const uint32_t k_lines = (row_bytes + 127u) / 128u;                 // 128-byte lines along K
+    const uint32_t kl0 = (uint32_t)L * BK * 2u / 128u;                  // first line past the prologue
+    const uint32_t b_touch = (seg_bytes + 127u) / 128u + 1u;            // touches per B row (any alignment)
+    const uint32_t per_line = rows_a + 64u * b_touch;                   // A rows + the 64 B rows of a K line
+    if (kl0 >= k_lines) return;
+    const uint32_t total = (k_lines - kl0) * per_line;
+    const uint32_t stride = parts * blockDim.x;
+    const uint8_t* a_panel = reinterpret_cast<const uint8_t*>(args.A) + m0 * K * 2u;
+    const uint8_t* b_panel = reinterpret_cast<const uint8_t*>(args.B) + n0 * 2u;
+    // address of touch `idx`: every address is inside A's rows [m0, m0 + rows_a) or B's rows
+    // [0, K) x columns [n0, n0 + cols_b) (out-of-range indexes are clamped onto the last line)
+    auto address = [&](uint32_t idx) __attribute__((always_inline)) -> const uint32_t* {
+        idx = idx < total ? idx : total - 1u;
+        const uint32_t kl = kl0 + idx / per_line, t = idx % per_line;
+        if (t < rows_a) {
+            const uint32_t off = kl * 128u < row_bytes - 4u ? kl * 128u : row_bytes - 4u;
+            return reinterpret_cast<const uint32_t*>(a_panel + (uint64_t)t * row_bytes + off);
+        }
+        const uint32_t u = t - rows_a, kr = u / b_touch, c = u % b_touch;
+        const uint64_t k = (uint64_t)kl * 64u + kr < K ? (uint64_t)kl * 64u + kr : K - 1u;
+        const uint32_t off = c * 128u < seg_bytes - 4u ? c * 128u : seg_bytes - 4u;
+        return reinterpret_cast<const uint32_t*>(b_panel + k * N * 2u + off);
+    };
+    uint32_t sink = 0;
+    for (uint32_t base = part * blockDim.x + threadIdx.x; base < total; base += 8u * stride) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *address(base + (uint32_t)u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sink ^= v[u];
+    }
+    asm volatile("" ::"v"(sink));  // the loads are the point; keep them
+}
+
 template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI = 0>
 __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) {
     using T = GemmTraits<DT, BM, BN, BK, L, WGN, EPI>;
@@ -88,6 +154,10 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     const uint32_t k_blocks = args.k_blocks;
     const uint32_t wid = worker_of_workgroup(blockIdx.x, args.P, args.num_xcd, args.num_active);
     uint32_t stress_ctr = 0;  // race-detection build only (TSG_STRESS)
+    if (args.prefetch && wid >= args.num_active) {  // a worker without a tile (uniform per workgroup)
+        warm_l2_for_xcd<BM, BN, BK, L>(args);
+        return;
+    }
 
     // ---- DMA source offsets (bytes from the slab origin) = lane part + uniform part ----
     // Instruction q of this wave fills 16-byte LDS positions p = qe*64 + lane,

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "tsgemm.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tsgemm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tsgemm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -271,3 +271,38 @@ def test_worker_numbering_is_a_balanced_permutation(P, X):
             assert np.all(ids[:len(act)] < A)                                 # active slots first
     with pytest.raises(tsg.TsgemmError):
         tsg.worker_numbering(P, X, 0)
+
+
+def test_set_l2_prefetch_validation_and_info():
+    lib = tsg.load()
+    p = tsg.Plan(1024, 1024, 1024, "fp16", 128, 128, 32, 4, 3)
+    assert p.info()["l2_prefetch"] == 1  # on by default for fp16/bf16 plans
+    assert lib.tsgemm_set_l2_prefetch(p._h, 0) == tsg.OK and p.info()["l2_prefetch"] == 0
+    assert lib.tsgemm_set_l2_prefetch(p._h, 1) == tsg.OK and p.info()["l2_prefetch"] == 1
+    for bad in (-1, 2):
+        assert lib.tsgemm_set_l2_prefetch(p._h, bad) == tsg.EINVAL
+        assert "0 or 1" in tsg.last_error()
+    assert lib.tsgemm_set_l2_prefetch(None, 1) == tsg.EINVAL
+    assert tsg.Plan(1024, 1024, 1024, "fp16", 128, 128, 32, 4, 3, l2_prefetch=False).info()["l2_prefetch"] == 0
+    mx = tsg.Plan(512, 512, 512, "mxfp8", 256, 256, 128, 2, 2)
+    assert mx.info()["l2_prefetch"] == 0
+    assert lib.tsgemm_set_l2_prefetch(mx._h, 0) == tsg.OK
+    assert lib.tsgemm_set_l2_prefetch(mx._h, 1) == tsg.EUNSUPPORTED
+
+
+def test_info_struct_layout_matches_header(tmp_path):
+    """The binding's tsgemm_info mirrors the C struct: every field at the
+    offset, and the struct at the size, a C compiler gives the header's."""
+    fields = [name for name, _ in tsg.Info._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"tsgemm.h\"\nint main(void) {\n"
+                   + "".join(f'    printf("{f} %zu\\n", offsetof(tsgemm_info, {f}));\n' for f in fields)
+                   + '    printf("sizeof %zu\\n", sizeof(tsgemm_info));\n    return 0;\n}\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for f in fields:
+        assert int(out[f]) == getattr(tsg.Info, f).offset, f
+    assert int(out["sizeof"]) == ctypes.sizeof(tsg.Info)

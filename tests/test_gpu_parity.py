@@ -394,6 +394,37 @@ def test_schedule_options_parity_256(cm, cs, waves):
     _check_close(C.double().numpy(), _bits_to_f64(ref_bits, "bf16"), "options 256")
 
 
+# ---------------------------------------------------------------- L2 warming by workers without a tile
+# (M, N, K, dtype, (bm, bn, bk), S, P, xcd_remap, waves, column_major, cluster_size); every case has
+# fewer tiles than workers, so some workers warm the L2 instead of leaving
+PREFETCH_CASES = [
+    (1024, 1024, 1024, "fp16", (128, 128, 32), 3, 0, True, 0, False, 1),     # the 1024^3 workload's plan
+    (1000, 1016, 992, "fp16", (128, 128, 32), 3, 0, True, 0, False, 1),      # ragged edges, K ends mid-line
+    (7 * 128 - 40, 6 * 128, 256, "fp16", (128, 128, 64), 2, 0, True, 0, True, 2),  # clusters, column-major
+    (2000, 1288, 4096, "bf16", (256, 256, 64), 2, 0, True, 8, False, 1),     # 8 waves
+    (1000, 1016, 992, "bf16", (128, 128, 32), 3, 100, False, 0, False, 1),   # no XCD renumbering, odd P
+    (640, 520, 64, "fp16", (128, 128, 32), 3, 0, True, 0, False, 1),         # K within the prologue: nothing to warm
+]
+
+
+@pytest.mark.parametrize("case", PREFETCH_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{c[3]}_P{c[6]}_w{c[8]}")
+def test_l2_warming_leaves_c_bit_identical(case):
+    M, N, K, dtype, (bm, bn, bk), S, P, xcd, waves, cm, cs = case
+    print(f"[case] l2 warming {case}", flush=True)
+    A, B = make_inputs(M, N, K, dtype, "uniform" if dtype == "fp16" else "normal_sqrtk", 600 + K % 97)
+    outs = []
+    for pf in (False, True):
+        plan = tsg.Plan(M, N, K, dtype, bm, bn, bk, 4, S, num_workgroups=P, xcd_remap=xcd, waves=waves,
+                        column_major=cm, cluster_size=cs, l2_prefetch=pf)
+        assert plan.info()["l2_prefetch"] == int(pf)
+        C, guard = _run(plan, A, B, dtype, guard=64)
+        assert torch.isnan(guard.float()).all(), "write past the end of C"
+        outs.append(C)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref_bits, _ = oracle.reference_c(A.double().numpy(), B.double().numpy(), FMT[dtype])
+    _check_close(outs[1].double().numpy(), _bits_to_f64(ref_bits, dtype), "l2 warming")
+
+
 # ---------------------------------------------------------------- chunked epilogue
 EPI_TILES = [(128, 128, 32, 5), (128, 128, 64, 5), (256, 256, 32, 4), (256, 256, 64, 3)]
 
