@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     TileScheduler ld;
     ld.setup(args.P, args.m_blocks, args.n_blocks, args.group, args.cluster, args.col_major);
     ld.init(wid);
-    uint32_t ld_k = 0, ld_slot = 0;
+    uint32_t ld_k = 0;
     uint32_t a_dec = 0, b_cap = 0, b_last = 0;
     const uint32_t M32 = (uint32_t)args.M;
     const uint64_t b_step = (uint64_t)BK * N * 2u;
@@ -263,25 +263,54 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         rs_b = rsrc_words_u64(reinterpret_cast<uint64_t>(args.B) + (live ? (uint64_t)n0 * 2u : 0u),
                               k_blocks == 1u ? b_last : b_cap);
     };
-    // step the loader to the slab after, once every DMA of the current one
-    // has been issued
+    // Step the loader to the slab after, once every DMA of the current one
+    // has been issued.  With one wave per SIMD a wave issues at most one
+    // instruction every four cycles, so a 16-cycle MFMA leaves room for three
+    // others before the next MFMA can go; a longer run of scalar work in one
+    // gap stalls the matrix core.  The step is therefore cut into pieces of at
+    // most three scalar instructions, one per gap, in this order:
+    //   0: A's origin and range;  1: B's origin;  2: the LDS target (wraps to
+    //   slot 0 after slot L-1);  3: B's range for the next slab (the tile's
+    //   last slab stops at the end of B);  4: the slab count, and at a tile's
+    //   end (rare, branched over) the next tile's descriptors.
+    // Each piece starts and ends with an empty volatile asm on the registers
+    // it changes: volatile asm keeps its order with the MFMAs (volatile asm
+    // too), so the compiler can neither hoist a piece's work above the MFMA
+    // before its gap nor sink it past the MFMA after.
+    const uint32_t dma_first = dma_lds, dma_wrap = dma_lds + (L - 1) * T::STAGE;
+    const uint32_t k_before_last = k_blocks - 2u;  // wraps for k_blocks = 1: every step then starts a tile
+    constexpr int kAdvPieces = 5;
+    auto adv_piece = [&](auto p_c) __attribute__((always_inline)) {
+        constexpr int p = decltype(p_c)::value;
+        if constexpr (p == 0) {
+            asm volatile("" : "+s"(rs_a));
+            add64(rs_a, BK * 2u);
+            rs_a.z -= (int)a_dec;
+            asm volatile("" : "+s"(rs_a));
+        } else if constexpr (p == 1) {
+            asm volatile("" : "+s"(rs_b));
+            add64(rs_b, b_step);
+            asm volatile("" : "+s"(rs_b));
+        } else if constexpr (p == 2) {
+            asm volatile("" : "+s"(dma_lds));
+            dma_lds = dma_lds == dma_wrap ? dma_first : dma_lds + T::STAGE;
+            asm volatile("" : "+s"(dma_lds));
+        } else if constexpr (p == 3) {
+            asm volatile("" : "+s"(rs_b), "+s"(ld_k));
+            rs_b.z = (int)(ld_k == k_before_last ? b_last : b_cap);
+            asm volatile("" : "+s"(rs_b));
+        } else {
+            asm volatile("" : "+s"(ld_k));
+            if (__builtin_expect(++ld_k == k_blocks, 0)) {
+                ld_k = 0;
+                ld.next_tile();
+                tile_ranges();
+            }
+            asm volatile("" : "+s"(ld_k), "+s"(rs_a), "+s"(rs_b));
+        }
+    };
     auto slab_advance = [&]() __attribute__((always_inline)) {
-        add64(rs_a, BK * 2u);
-        rs_a.z -= (int)a_dec;
-        add64(rs_b, b_step);
-        if (++ld_slot == (uint32_t)L) {
-            ld_slot = 0;
-            dma_lds -= (L - 1) * T::STAGE;
-        } else {
-            dma_lds += T::STAGE;
-        }
-        if (++ld_k == k_blocks) {
-            ld_k = 0;
-            ld.next_tile();
-            tile_ranges();
-        } else {
-            rs_b.z = (int)(ld_k + 1u == k_blocks ? b_last : b_cap);
-        }
+        static_for<0, kAdvPieces>([&](auto p_c) __attribute__((always_inline)) { adv_piece(p_c); });
     };
     tile_ranges();
     // One DMA in one piece (prologue): its LDS target is written to M0 inside
@@ -446,17 +475,31 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // EPH: 0 no stores, 1 the current tile's stores of blocks fm < kEpiFirst
     // (its last k-step), 2 the previous tile's other stores (the tile's first
     // k-step, whose MFMAs start from zero).
-    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c, auto eph_c) __attribute__((always_inline)) {
+    // One k-step per slab: the stage the k-steps read, stepped along by the
+    // k-step itself (a compare and select in an MFMA gap of its own, pinned
+    // like the loader's pieces) instead of recomputed from the slab count.
+    // It starts one slot behind: the first k-step steps it to slot 1.
+    uint32_t st_rd = 0;
+    auto next_stage = [](uint32_t& st) __attribute__((always_inline)) {
+        asm volatile("" : "+s"(st));
+        st = st == (L - 1) * T::STAGE ? 0u : st + T::STAGE;
+        asm volatile("" : "+s"(st));
+    };
+    // STP: read from st_rd, stepped in gap START - 2 (before the first
+    // address add that uses it), instead of from read_st.
+    auto kstep = [&](auto cur_c, auto last_c, auto ksn_c, uint32_t read_st, auto same_c, auto eph_c, auto stp_c) __attribute__((always_inline)) {
         constexpr int EPH = decltype(eph_c)::value;
         constexpr int CUR = decltype(cur_c)::value;
         constexpr bool SAME = decltype(same_c)::value;
         constexpr int NXT = SAME ? CUR : 1 - CUR;
         constexpr bool LAST = decltype(last_c)::value;
+        constexpr bool STP = decltype(stp_c)::value;
         constexpr int NSTEP = FM * FN;
         constexpr int S0 = LAST ? 2 : 0;                   // MFMAs issued before the barrier
         constexpr int START = S0 > kGap ? S0 : kGap;       // first step with memory operations
         constexpr int AVAIL = NSTEP - START - 1;
         static_assert(AVAIL >= 2, "k-step too short for its memory operations");
+        static_assert(!STP || START >= 2, "the stage step needs a gap before the first address add");
         static_assert(LAST ? T::DF <= AVAIL + 1 : NL - T::DF <= AVAIL + 1, "every DMA of a slab needs a gap");
         // LAST issues DMAs [0, DF) of slab phase+L; the following first k-step
         // of the next slab issues [DF, NL) of the same slab
@@ -488,12 +531,13 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                 lds_barrier();                                       // ... for every wave; stage phase free
                 stress_pause<1>(wave, stress_ctr);
             }
+            if constexpr (STP && s == START - 2) next_stage(st_rd);
             if constexpr (s + 1 >= START) {
                 // addresses of the reads issued in the next step
                 constexpr int p0 = (s + 1 - START) * PER;
                 constexpr int p1 = p0 + PER < QR ? p0 + PER : QR;
                 static_for<p0, (p1 > p0 ? p1 : p0)>([&](auto q_c) __attribute__((always_inline)) {
-                    prep_op(ksn_c, q_c, read_st);
+                    prep_op(ksn_c, q_c, STP ? st_rd : read_st);
                 });
             }
             if constexpr (s >= START) {
@@ -505,9 +549,15 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                     read_op(std::integral_constant<int, NXT>{}, q_c);
                 });
             }
-            // after this gap's DMA: with short k-steps the last DMA can sit in
-            // the gap ADV itself
-            if constexpr ((kSplitAdvance ? !LAST : LAST) && s == ADV) slab_advance();
+            // after this gap's DMA (with short k-steps the last DMA can sit in
+            // the gap ADV itself): piece p of the loader's step in gap ADV + p,
+            // the pieces that do not fit before the k-step's end in its last gap
+            if constexpr (kSplitAdvance ? !LAST : LAST) {
+                static_for<0, kAdvPieces>([&](auto p_c) __attribute__((always_inline)) {
+                    constexpr int p = decltype(p_c)::value;
+                    if constexpr (s == (ADV + p < NSTEP - 1 ? ADV + p : NSTEP - 1)) adv_piece(p_c);
+                });
+            }
             if constexpr (EPH == 1) {
                 static_for<0, kEpiFirst>([&](auto fm_c) __attribute__((always_inline)) {
                     static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
@@ -530,7 +580,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         });
         if constexpr (SAME) {
             gap_nops();
-            set_addr(ksn_c, read_st);
+            set_addr(ksn_c, STP ? st_rd : read_st);
             static_for<0, R>([&](auto r_c) __attribute__((always_inline)) { read_op(cur_c, r_c); });
         }
     };
@@ -675,31 +725,28 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
             // rotated: the tile's first k-step, then (last k-step of slab k,
             // first k-step of slab k+1) pairs, then its last k-step; one code
             // path per tile, so the accumulators stay put
-            kstep(I0{}, FALSE_{}, I1{}, (phase % L) * T::STAGE, FALSE_{}, I2{});
+            kstep(I0{}, FALSE_{}, I1{}, (phase % L) * T::STAGE, FALSE_{}, I2{}, FALSE_{});
             for (uint32_t k = 0; k + 1u < k_blocks; ++k, ++phase) {
-                kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{});
-                kstep(I0{}, FALSE_{}, I1{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{});
+                kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{}, FALSE_{});
+                kstep(I0{}, FALSE_{}, I1{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{}, FALSE_{});
             }
             epi_state();  // after the previous tile's last stores
-            kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I1{});
+            kstep(I1{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I1{}, FALSE_{});
             ++phase;
         } else if constexpr (KS == 2) {
             for (uint32_t k = 0; k < k_blocks; ++k, ++phase) {
                 const uint32_t st_cur = (phase % L) * T::STAGE;
                 const uint32_t st_next = ((phase + 1u) % L) * T::STAGE;
-                kstep(I0{}, FALSE_{}, I1{}, st_cur, FALSE_{}, I0{});
-                kstep(I1{}, TRUE_{}, I0{}, st_next, FALSE_{}, I0{});
+                kstep(I0{}, FALSE_{}, I1{}, st_cur, FALSE_{}, I0{}, FALSE_{});
+                kstep(I1{}, TRUE_{}, I0{}, st_next, FALSE_{}, I0{}, FALSE_{});
             }
         } else {
             uint32_t k = 0;
-            for (; k + 1u < k_blocks; k += 2u, phase += 2u) {
-                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, FALSE_{}, I0{});
-                kstep(I1{}, TRUE_{}, I0{}, ((phase + 2u) % L) * T::STAGE, FALSE_{}, I0{});
+            for (; k + 1u < k_blocks; k += 2u) {
+                kstep(I0{}, TRUE_{}, I0{}, 0u, FALSE_{}, I0{}, TRUE_{});
+                kstep(I1{}, TRUE_{}, I0{}, 0u, FALSE_{}, I0{}, TRUE_{});
             }
-            if (k < k_blocks) {
-                kstep(I0{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE, TRUE_{}, I0{});
-                ++phase;
-            }
+            if (k < k_blocks) kstep(I0{}, TRUE_{}, I0{}, 0u, TRUE_{}, I0{}, TRUE_{});
         }
         if constexpr (kEpiInterleave)
             pend = true;
