@@ -311,6 +311,82 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         slab_desc();
         slab_advance();
     };
+    // In the main loop the same two steps go out in pieces, each between
+    // empty volatile asm statements on the registers it reads and writes: a
+    // wave issues one instruction every four cycles and the scaled MFMA keeps
+    // the matrix core busy for 64, so fifteen instructions fit in a gap, and
+    // the compiler would otherwise hoist the descriptor work into the gap
+    // before the k-step's first MFMA next to the loop's own scalar work.
+    //   desc 0: LDS targets and whether the slab starts a scale group;
+    //   desc 1..4: the A, B, SFA and SFB descriptors;
+    //   adv 0: the A and B origins and ranges;  adv 1: the scale origins and
+    //   ranges and the group count;  adv 2: LDS slot, slab count, next tile.
+    auto desc_piece = [&](auto p_c) __attribute__((always_inline)) {
+        constexpr int p = decltype(p_c)::value;
+        if constexpr (p == 0) {
+            asm volatile("" : "+s"(ld_lds), "+s"(ld_k));
+            dma_lds = ld_lds;
+            sc_issue = ld_live && (ld_k % T::SG) == 0;
+            sc_lds = __builtin_amdgcn_readfirstlane(lds_base + T::SC_OFF + (ld_grp & 1u) * T::SC_ENTRY + wave * 64u * T::SC_ROW);
+            asm volatile("" : "+s"(dma_lds), "+s"(sc_lds));
+        } else if constexpr (p == 1) {
+            asm volatile("" : "+s"(a_ptr), "+s"(a_num));
+            rs_a = rsrc_words_u64(a_ptr, a_num);
+            asm volatile("" : "+s"(rs_a));
+        } else if constexpr (p == 2) {
+            asm volatile("" : "+s"(b_ptr), "+s"(b_num));
+            rs_b = rsrc_words_u64(b_ptr, b_num);
+            asm volatile("" : "+s"(rs_b));
+        } else if constexpr (p == 3) {
+            asm volatile("" : "+s"(sa_ptr), "+s"(sa_num));
+            rs_sa = rsrc_words_u64(sa_ptr, sa_num);
+            asm volatile("" : "+s"(rs_sa));
+        } else {
+            asm volatile("" : "+s"(sb_ptr), "+s"(sb_num));
+            rs_sb = rsrc_words_u64(sb_ptr, sb_num);
+            asm volatile("" : "+s"(rs_sb));
+        }
+    };
+    auto adv_piece = [&](auto p_c) __attribute__((always_inline)) {
+        constexpr int p = decltype(p_c)::value;
+        if constexpr (p == 0) {
+            asm volatile("" : "+s"(a_ptr), "+s"(b_ptr), "+s"(a_num), "+s"(b_num));
+            a_ptr += (uint32_t)T::BK;
+            a_num -= dec;
+            b_ptr += (uint32_t)T::BK;
+            b_num -= dec;
+            asm volatile("" : "+s"(a_ptr), "+s"(b_ptr), "+s"(a_num), "+s"(b_num));
+        } else if constexpr (p == 1) {
+            asm volatile("" : "+s"(sa_ptr), "+s"(sb_ptr), "+s"(sa_num), "+s"(sb_num));
+            ld_grp += sc_issue ? 1u : 0u;
+            if constexpr (PACKED) {
+                if (sc_issue) {
+                    sa_ptr += kGroupBytes;
+                    sb_ptr += kGroupBytes;
+                }
+            } else {
+                sa_ptr += (uint32_t)T::BK / 32u;
+                sa_num -= sdec;
+                sb_ptr += (uint32_t)T::BK / 32u;
+                sb_num -= sdec;
+            }
+            asm volatile("" : "+s"(sa_ptr), "+s"(sb_ptr), "+s"(sa_num), "+s"(sb_num));
+        } else {
+            asm volatile("" : "+s"(ld_lds), "+s"(ld_slot), "+s"(ld_k));
+            if (++ld_slot == (uint32_t)L) {
+                ld_slot = 0;
+                ld_lds -= (L - 1) * T::STAGE;
+            } else {
+                ld_lds += T::STAGE;
+            }
+            if (__builtin_expect(++ld_k == k_blocks, 0)) {
+                ld_k = 0;
+                ld.next_tile();
+                tile_ranges();
+            }
+            asm volatile("" : "+s"(ld_lds), "+s"(ld_slot), "+s"(ld_k));
+        }
+    };
     tile_ranges();
     // DMA q of a slab in issue order: A and B chunks [0, DF), then (only when
     // the slab starts a scale group) the group's scale DMAs, SFA then SFB, then
@@ -457,13 +533,14 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
         constexpr int DPER = D ? (D + AVAIL - 1) / AVAIL : 0;
         constexpr int PER = (R + AVAIL - 1) / AVAIL;
         static_assert(AVAIL * PER >= R && (D == 0 || AVAIL * DPER >= D), "k-step too short for its memory operations");
-        // LAST: the next slab's descriptors after the first MFMA (scalar only;
-        // the DMAs themselves wait for the barrier), the loader's step after
-        // the k-step's last DMA (any later step works: the DMAs of this slab
-        // use the descriptors formed at step 0)
-        constexpr int ADV = START + (D ? (D + DPER - 1) / DPER : 0) < NSTEP - 1 ? START + (D ? (D + DPER - 1) / DPER : 0)
-                                                                              : NSTEP - 1;
-        if constexpr (!LAST) set_addr(ksn_c, read_st, read_scb);
+        static_assert(START >= 2, "the first k-step's addresses need a gap before its first read");
+        // the scale descriptors after the barrier's gap, before the slab's
+        // first scale DMA (issue position DF); the loader's three pieces
+        // after the first k-step's DMAs
+        constexpr int kScaleDesc = START + 1;
+        constexpr int kAdvGap = NSTEP - 6;
+        static_assert(!LAST || D == 0 || START + T::DF / DPER >= kScaleDesc + 2, "scale descriptors before their DMAs");
+        static_assert(LAST || D == 0 || START + (D + DPER - 1) / DPER <= kAdvGap, "the loader steps after the first k-step's DMAs");
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
             constexpr int fm = s / F, fn = s % F;
@@ -473,8 +550,24 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
                 mfma_mx32_clear(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
             else
                 mfma_mx32(acc[fm][fn], b8, a8, sb[CUR][fn], sa[CUR][fm]);
-            if constexpr (LAST && s == 0) slab_desc();
-            if constexpr (LAST && s == ADV) slab_advance();
+            // LAST: the slab's descriptors, A and B before its first DMA, the
+            // scale descriptors before its first scale DMA; the slab's first
+            // k-step (!LAST): the loader's step, after that k-step's DMAs of
+            // the previous slab (they use the descriptors already formed)
+            if constexpr (LAST && s == 0) {
+                desc_piece(std::integral_constant<int, 0>{});
+                desc_piece(std::integral_constant<int, 1>{});
+            }
+            if constexpr (LAST && s == 1) desc_piece(std::integral_constant<int, 2>{});
+            if constexpr (LAST && s == kScaleDesc) desc_piece(std::integral_constant<int, 3>{});
+            if constexpr (LAST && s == kScaleDesc + 1) desc_piece(std::integral_constant<int, 4>{});
+            if constexpr (!LAST && s >= kAdvGap && s < kAdvGap + 3)
+                adv_piece(std::integral_constant<int, (s >= kAdvGap ? s - kAdvGap : 0)>{});
+            if constexpr (!LAST && s == START - 1) {
+                asm volatile("" : "+s"(read_st), "+s"(read_scb));
+                set_addr(ksn_c, read_st, read_scb);
+                asm volatile("" : "+v"(ra[0]), "+v"(ra[1]), "+v"(rb[0]), "+v"(rb[1]), "+v"(rsa), "+v"(rsb));
+            }
             if constexpr (LAST && s == S0 - 1) {
                 stress_pause<0>(wave, stress_ctr);
                 wait_vm<0>();    // slab phase+1 (and its scale group) has landed
@@ -517,11 +610,13 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
 
     // prologue: slabs 0..L-1 in flight, the first k-step's fragments read
     for (int s = 0; s < L; ++s) {
-        next_slab();
-        if (s + 1 < L)
+        if (s + 1 < L) {
+            next_slab();
             static_for<0, NSC + ND>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
-        else  // the last prologue slab's chunks [DF, ND) follow in the first k-step
+        } else {  // the last prologue slab's chunks [DF, ND) and the loader's step follow in the first k-step
+            slab_desc();
             static_for<0, T::DF + NSC>([&](auto q_c) __attribute__((always_inline)) { dma_op(q_c); });
+        }
     }
     stress_pause<3>(wave, stress_ctr);
     wait_vm<0>();
