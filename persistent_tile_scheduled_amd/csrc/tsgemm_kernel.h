@@ -519,7 +519,11 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int ADV = MEM_END < NSTEP - 1 ? MEM_END : NSTEP - 1;
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
-            constexpr int fm = s / FN, fn = s % FN;
+            // row blocks fm in order; within a row the B blocks forward on even
+            // rows and backward on odd ones, so consecutive MFMAs share an
+            // operand at every row change too (fewer operand bits switch:
+            // measured ~1% more MFMA work per joule on random bf16 data)
+            constexpr int fm = s / FN, fn = (fm & 1) ? FN - 1 - s % FN : s % FN;
             const i16x8 bv = __builtin_shufflevector(fb[CUR][fn][0], fb[CUR][fn][1], 0, 1, 2, 3, 4, 5, 6, 7);
             if constexpr (EPH == 2)
                 mfma16x16x32_clear<DT>(acc[fm][fn], bv, fa[CUR][fm]);
