@@ -43,6 +43,26 @@ constexpr int dma_spacing(int bk) { return TSG_DMA_SPACING > 0 ? TSG_DMA_SPACING
 #endif
 constexpr int kGap = TSG_GAP;  // MFMAs between the last read of a fragment set and its refill
 
+// Cache policy of the fp16/bf16 kernels' stores of C: nt (bit 1,
+// non-temporal) | sc1 (bit 4, device scope, written through).  A wave of
+// 256x256 tiles has each XCD write 32 tiles = 4 MiB of C, as much as its whole
+// L2; stored as ordinary lines they evicted the A and B slabs the XCD's other
+// workgroups were still reading, which then came back from beyond the L2 a
+// second time.  Streamed past the L2 they do not: at 8192^3 the reads from
+// beyond the L2 fall to the tiling's floor (each XCD fetching its 4 A and 8 B
+// panels once per wave).  Each store writes 64 contiguous bytes of 16 rows.
+#ifndef TSG_C_CPOL
+#define TSG_C_CPOL 18
+#endif
+// The block-scaled kernel keeps ordinary stores: its 32x32 accumulator layout
+// writes only 32 contiguous bytes per row and store, and written through
+// unmerged those partial lines nearly double the bytes written, while its fp8
+// slabs, half the bytes of fp16 ones, already come from beyond the L2 close to
+// once per XCD and wave.
+#ifndef TSG_MX_C_CPOL
+#define TSG_MX_C_CPOL 0
+#endif
+
 #ifndef TSG_STRESS
 #define TSG_STRESS 0  // 1: race-detection build, pauses at every synchronisation site (tests only)
 #endif

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         const uint32_t y0 = cvt_pk<DT>(y[0], y[1]), y1 = cvt_pk<DT>(y[2], y[3]);
         const u32x4 v = swap ? u32x4{y0, y1, x0, x1} : u32x4{x0, x1, y0, y1};
         const bool ok = row0 + fm * 16 < e_rows && col0 + 32u * t < e_cols;
-        __builtin_amdgcn_raw_buffer_store_b128(v, e_rc, (ok ? lane_off : 0x80000000u) + t * 64, fm * 16 * N * 2, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, e_rc, (ok ? lane_off : 0x80000000u) + t * 64, fm * 16 * N * 2, TSG_C_CPOL);
     };
 
     // One 32-deep k-step: FM*FN MFMAs (fm-major) from register set CUR,
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                         chunk + r * 128u + ((j ^ (r & 7u)) * 16u)));
                     const uint32_t col = (uint32_t)c * EPI + 8u * j;
                     const bool ok = r < rows_left && col < cols_left;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? (r * N + col) * 2u : 0x80000000u, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, ok ? (r * N + col) * 2u : 0x80000000u, 0, TSG_C_CPOL);
                     store_gap();
                 });
                 stress_pause<5>(wave, stress_ctr);
@@ -690,7 +690,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
                 const u32x4 v = swap ? u32x4{y0, y1, x0, x1} : u32x4{x0, x1, y0, y1};
                 const bool ok = row_ok && col0 + 32u * t < cols_left;
                 __builtin_amdgcn_raw_buffer_store_b128(v, rc, (ok ? lane_off : 0x80000000u) + t * 64,
-                                                       fm * 16 * N * 2, 0);
+                                                       fm * 16 * N * 2, TSG_C_CPOL);
                 // the store's data registers are read after it issues: two wait
                 // states before the next conversion overwrites them
                 store_gap();

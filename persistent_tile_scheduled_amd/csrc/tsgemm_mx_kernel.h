@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256, 1) void tsgemm_mx_kernel(MxArgs args) {
                          cvt_pk<DT_BF16>(x[8 * hs + 4], x[8 * hs + 5]), cvt_pk<DT_BF16>(x[8 * hs + 6], x[8 * hs + 7])};
         const bool ok = row0 + fm * 32 < e_rows && col0 + 32u * fn + 16u * hs < e_cols;
         __builtin_amdgcn_raw_buffer_store_b128(v, e_rc, (ok ? lane_off : 0x80000000u) + (fn * 32 + 16 * hs) * 2,
-                                               fm * 32 * N * 2, 0);
+                                               fm * 32 * N * 2, TSG_MX_C_CPOL);
     };
 
     // One 64-deep k-step: 16 MFMAs (fm-major) from register set CUR, with the
