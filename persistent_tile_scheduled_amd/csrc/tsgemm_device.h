@@ -63,6 +63,15 @@ constexpr int kGap = TSG_GAP;  // MFMAs between the last read of a fragment set 
 #define TSG_MX_C_CPOL 0
 #endif
 
+// Cache policy of the LDS-DMA loads: sc0, so the L1 does not keep the lines.
+// A CU requests every byte of a slab once (the other workgroups sharing a
+// panel are on other CUs, and meet in the L2), so there is nothing to keep;
+// at 8192^3 this was 0.5% faster, elsewhere the same.  (nt, which also stops
+// the L2 keeping them, was 30-60% slower: the L2 is where slabs are shared.)
+#ifndef TSG_DMA_MOD
+#define TSG_DMA_MOD " sc0"
+#endif
+
 #ifndef TSG_STRESS
 #define TSG_STRESS 0  // 1: race-detection build, pauses at every synchronisation site (tests only)
 #endif
@@ -222,7 +231,7 @@ __device__ __forceinline__ i32x4 rsrc_words_u64(uint64_t a, uint32_t bytes) {
 // no asm operand asks the compiler for a value in M0.
 template <uint32_t OFF>
 __device__ __forceinline__ void dma16_at(uint32_t lds_base_addr, uint32_t voff, i32x4 rsrc) {
-    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen" TSG_DMA_MOD " lds"
                  ::"v"(voff), "s"(rsrc), "s"(lds_base_addr), "i"(OFF)
                  : "memory", "m0", "scc");
 }
@@ -235,7 +244,7 @@ __device__ __forceinline__ void set_m0(uint32_t lds_base_addr) {
     asm volatile("s_add_u32 m0, %0, %1" ::"s"(lds_base_addr), "i"(OFF) : "m0", "scc");
 }
 __device__ __forceinline__ void dma16_m0(uint32_t voff, i32x4 rsrc) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen" TSG_DMA_MOD " lds" ::"v"(voff), "s"(rsrc) : "memory");
 }
 
 }  // namespace tsg
