@@ -77,21 +77,33 @@ def recorded_traffic(workload: str, kind: str = "gemm"):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def _rows_for(run, M: int, target_s: float):
+    """Rows of C whose oracle product takes about target_s seconds, and the time
+    per row.  Calibrated twice: on 64 rows, whose time is dominated by starting
+    the oracle's threads, then on enough rows for ~2 s."""
+    rows = min(M, 64)  # enough rows to keep every oracle thread busy
+    t0 = time.perf_counter()
+    run(rows)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    r2 = int(min(M, rows * 2.0 / dt))
+    if r2 > rows:
+        t0 = time.perf_counter()
+        run(r2)
+        rows, dt = r2, max(time.perf_counter() - t0, 1e-4)
+    return int(max(8, min(M, rows * target_s / dt))), dt / rows
+
+
 def cpu_baseline(w, A, B, target_s: float = 15.0):
     """Time the oracle on the first R rows of C, R sized for ~target_s seconds;
     a whole product smaller than that is repeated to fill the window."""
     import numpy as np
     import oracle
     B64 = B.double().numpy()
-    rows = min(w.M, 64)  # enough rows to keep every oracle thread busy while calibrating
-    t0 = time.perf_counter()
-    oracle.gemm_f64(A[:rows].double().numpy(), B64)
-    dt = time.perf_counter() - t0
-    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-3))))
+    rows, per_row = _rows_for(lambda r: oracle.gemm_f64(A[:r].double().numpy(), B64), w.M, target_s)
     # a product too small to fill the window is repeated whole (the small shapes)
     reps = 1
     if rows == w.M:
-        reps = int(max(1, min(1000, target_s / max(dt * w.M / min(w.M, 64), 1e-4))))
+        reps = int(max(1, min(1000, target_s / max(per_row * w.M, 1e-4))))
     A64 = A[:rows].double().numpy()
     t0 = time.perf_counter()
     for _ in range(reps):
@@ -113,11 +125,7 @@ def cpu_baseline_mx(w, A, SFA, B, SFB, target_s: float = 15.0):
     """Time the MX oracle on the first R rows of C, R sized for ~target_s seconds."""
     import numpy as np
     import oracle
-    rows = min(w.M, 64)
-    t0 = time.perf_counter()
-    oracle.mx_gemm_f64(A[:rows], SFA[:rows], B, SFB)
-    dt = time.perf_counter() - t0
-    rows = int(max(8, min(w.M, rows * target_s / max(dt, 1e-3))))
+    rows, _ = _rows_for(lambda r: oracle.mx_gemm_f64(A[:r], SFA[:r], B, SFB), w.M, target_s)
     t0 = time.perf_counter()
     c = oracle.mx_gemm_f64(A[:rows], SFA[:rows], B, SFB)
     dt = time.perf_counter() - t0
