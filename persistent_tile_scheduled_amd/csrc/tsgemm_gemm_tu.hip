@@ -14,6 +14,12 @@ namespace {
 
 template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI>
 void launch_gemm(const GemmArgs& a, unsigned grid, hipStream_t s) {
+    if constexpr (pair_kernel(BM, BN, BK, WGN, EPI)) {
+        if (a.k_blocks >= 2u) {  // the paired kernel runs tiles of two slabs or more
+            hipLaunchKernelGGL((tsgemm_kernel<DT, BM, BN, BK, L, WGN, EPI, true>), dim3(grid), dim3(64 * 2 * WGN), 0, s, a);
+            return;
+        }
+    }
     hipLaunchKernelGGL((tsgemm_kernel<DT, BM, BN, BK, L, WGN, EPI>), dim3(grid), dim3(64 * 2 * WGN), 0, s, a);
 }
 

@@ -140,7 +140,17 @@ __device__ __forceinline__ void warm_l2_for_xcd(const GemmArgs& args) {
     asm volatile("" ::"v"(sink));  // the loads are the point; keep them
 }
 
-template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI = 0>
+#ifndef TSG_PAIR
+#define TSG_PAIR 1  // 0: no paired-k-step kernels (every plan runs the k-step-by-k-step order)
+#endif
+// The kernels that run each slab's two k-steps as MFMA pairs on one
+// accumulator (PAIR, below): 256x256x64 tiles, four waves, direct stores.
+// A plan runs them when its tiles have at least two slabs.
+constexpr bool pair_kernel(int bm, int bn, int bk, int wgn, int epi) {
+    return TSG_PAIR && TSG_EPI_INTERLEAVE && bm == 256 && bn == 256 && bk == 64 && wgn == 2 && epi == 0;
+}
+
+template <int DT, int BM, int BN, int BK, int L, int WGN, int EPI = 0, bool PAIR = false>
 __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) {
     using T = GemmTraits<DT, BM, BN, BK, L, WGN, EPI>;
     constexpr int FM = T::FM, FN = T::FN, KS = T::KS, NA = T::NA, NB = T::NB, NL = T::NL;
@@ -427,6 +437,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     // intact for 32+ cycles before the next conversion overwrites them (two
     // wait states are required, store_gap).
     constexpr bool kEpiInterleave = TSG_EPI_INTERLEAVE && KS == 2 && EPI == 0 && WGN == 2 && FM % 2 == 0 && FN % 2 == 0;
+    static_assert(!PAIR || (kEpiInterleave && FM == 8 && FN == 8), "paired k-steps: 256x256x64 tiles, four waves");
     // MFMAs issued between a block's last MFMA and the first read of its
     // accumulators: the MFMAs are asm the compiler cannot see, so the wait
     // for their results is placed here (3 MFMAs, 48+ cycles)
@@ -595,6 +606,155 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     using TRUE_ = std::integral_constant<bool, true>;
     using FALSE_ = std::integral_constant<bool, false>;
 
+    // ---- paired k-steps (PAIR) ----
+    // Each slab's two 32-deep k-steps go to every accumulator as two MFMAs in
+    // a row: (k-step 0, k-step 1) of block (fm, fn), then the next block.  An
+    // MFMA whose accumulator input is the previous MFMA's result takes it from
+    // the matrix core's forwarding path instead of the register file, and on
+    // random data the board's power limit then allows ~4.7% more MFMA work
+    // (microbenchmark of the two orders at the limit).  Every accumulator still
+    // sees its k-steps in K order, so C is the k-step-by-k-step order's bit
+    // for bit.
+    // A slab runs in two phases of FM*FN MFMAs: phase 1 on column blocks
+    // fn < FN/2, phase 2 (which opens with the slab barrier, as the last
+    // k-step does above) on fn >= FN/2, row blocks in order in both.  So the
+    // fragments of both k-steps fit the registers of the two sets above:
+    //   B blocks fn >= FN/2 are read in phase 1 (from this slab), those below
+    //   in phase 2 (from the next slab), each half while the other is in use;
+    //   A row block fm is last read by row fm of phase 2, so blocks
+    //   fm < kPA2 are refilled from the next slab there, kGap MFMAs after
+    //   that row, and the rest early in the next phase 1.
+    // Phase 2 forms the next slab's LDS addresses, issues DMAs [0, DF) of slab
+    // phase+L into the stage phase 1 finished reading, and (EPH 1, a tile's
+    // last slab) stores column blocks fn < FN/2, final since phase 1; phase 1
+    // issues DMAs [DF, NL) and the loader's step, and (EPH 2, a tile's first
+    // slab) stores the previous tile's blocks fn >= FN/2 before phase 2
+    // overwrites them.  CLR: the tile's first slab (zero accumulator inputs).
+    constexpr int kPA2 = FM / 2;              // A row blocks refilled in phase 2
+    constexpr int kPR2B = 2 * FN;             // phase 2: B reads (fn < FN/2, both k-steps and halves)
+    constexpr int kPR2A = 2 * kPA2;           // phase 2: A reads (fm < kPA2, both k-steps)
+    constexpr int kPR1A = 2 * (FM - kPA2);    // phase 1: A reads (fm >= kPA2)
+    constexpr int kPR1B = 2 * FN;             // phase 1: B reads (fn >= FN/2)
+    constexpr int kPStart = kGap > 2 ? kGap : 2;
+    constexpr int kPSteps = FM * FN;
+    // gap of phase 2's A read i (row block i/2): after the B reads, and kGap
+    // MFMAs after the row's last MFMA in this phase
+    constexpr auto p2a_gap = [](int i) constexpr {
+        int p = kPStart + kPR2B;
+        for (int j = 0; j <= i; ++j) {
+            const int e = (j / 2) * FN + FN - 1 + kGap;
+            p = p > e ? p : e;
+            if (j < i) ++p;
+        }
+        return p;
+    };
+    constexpr int kPEpi = FM * FN / 4;        // stores per epilogue half
+    constexpr int kPEpiGap = kPSteps - 2 * kPEpi + 1;
+    i16x8 pa[FM][2];     // A fragments [row block][k-step]
+    i16x4 pb[FN][2][2];  // B fragments [column block][k-step][half]
+    uint32_t pra[2], prb[FN];
+    auto p_addr_a = [&](auto k_c, uint32_t st) __attribute__((always_inline)) {
+        pra[decltype(k_c)::value] = lds_base + st + a_off[decltype(k_c)::value];
+    };
+    auto p_addr_b = [&](auto fn_c, uint32_t st) __attribute__((always_inline)) {
+        prb[decltype(fn_c)::value] = lds_base + st + b_off[decltype(fn_c)::value];
+    };
+    auto p_read_a = [&](auto fm_c, auto k_c) __attribute__((always_inline)) {
+        constexpr int fm = decltype(fm_c)::value, k = decltype(k_c)::value;
+        pa[fm][k] = __builtin_bit_cast(i16x8, *(const __attribute__((address_space(3))) u32x4*)(
+                                              (__attribute__((address_space(3))) uint8_t*)(uintptr_t)pra[k] + fm * 16 * (BK * 2)));
+    };
+    auto p_read_b = [&](auto fn_c, auto k_c, auto h_c) __attribute__((always_inline)) {
+        constexpr int fn = decltype(fn_c)::value, k = decltype(k_c)::value, h = decltype(h_c)::value;
+        pb[fn][k][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) uint8_t*)(uintptr_t)prb[fn] + (k * 32 + h * 4) * (BN * 2)));
+    };
+    // B read r of a phase (column blocks from fn0), A read i (row blocks from fm0)
+    auto p_read_b_op = [&](auto fn0_c, auto r_c) __attribute__((always_inline)) {
+        constexpr int r = decltype(r_c)::value;
+        p_read_b(std::integral_constant<int, decltype(fn0_c)::value + r / 4>{}, std::integral_constant<int, (r / 2) % 2>{},
+                 std::integral_constant<int, r % 2>{});
+    };
+    auto p_read_a_op = [&](auto fm0_c, auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        p_read_a(std::integral_constant<int, decltype(fm0_c)::value + i / 2>{}, std::integral_constant<int, i % 2>{});
+    };
+    // the next slab's LDS addresses (phase 2, and the prologue)
+    auto p_addr_op = [&](auto q_c, uint32_t st) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;  // B blocks < FN/2, A (k-steps 0, 1), B blocks >= FN/2
+        if constexpr (q < FN / 2)
+            p_addr_b(std::integral_constant<int, q>{}, st);
+        else if constexpr (q < FN / 2 + 2)
+            p_addr_a(std::integral_constant<int, q - FN / 2>{}, st);
+        else
+            p_addr_b(std::integral_constant<int, q - 2>{}, st);
+    };
+    auto pstep = [&](auto ph_c, auto clr_c, auto eph_c, uint32_t st_next) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph_c)::value, EPH = decltype(eph_c)::value;
+        constexpr bool CLR = decltype(clr_c)::value, LAST = PH == 2;
+        constexpr int NSTEP = kPSteps;
+        constexpr int S0 = LAST ? 2 : 0;
+        constexpr int START = kPStart;
+        constexpr int AVAIL = NSTEP - START - 1;
+        constexpr int D = LAST ? T::DF : NL - T::DF;
+        constexpr int D0 = LAST ? 0 : T::DF;
+        constexpr int DS = D ? (AVAIL / D < dma_spacing(BK) ? (AVAIL / D > 0 ? AVAIL / D : 1) : dma_spacing(BK)) : 1;
+        constexpr int DMA_END = D ? START + (D - 1) * DS + 1 : 0;
+        constexpr int READ_END = LAST ? p2a_gap(kPR2A - 1) + 1 : START + kPR1A + kPR1B;
+        constexpr int MEM_END = DMA_END > READ_END ? DMA_END : READ_END;
+        constexpr int ADV = MEM_END < NSTEP - 1 ? MEM_END : NSTEP - 1;
+        static_assert(LAST ? p2a_gap(kPR2A - 1) < NSTEP && START + kPR2B <= p2a_gap(0) : READ_END <= NSTEP,
+                      "every read of a phase needs a gap");
+        static_assert(D <= AVAIL + 1 && kPEpiGap >= kEpiLag, "phase too short for its memory operations");
+        static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            constexpr int pr = s / 2, kk = s % 2;  // MFMA pair, k-step within the slab
+            constexpr int fm = pr / (FN / 2), j = pr % (FN / 2);
+            constexpr int fn = (LAST ? FN / 2 : 0) + ((fm & 1) ? FN / 2 - 1 - j : j);
+            const i16x8 bv = __builtin_shufflevector(pb[fn][kk][0], pb[fn][kk][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (CLR && kk == 0)
+                mfma16x16x32_clear<DT>(acc[fm][fn], bv, pa[fm][kk]);
+            else
+                mfma16x16x32<DT>(acc[fm][fn], bv, pa[fm][kk]);
+            if constexpr (LAST && s == S0 - 1) {
+                stress_pause<0>(wave, stress_ctr);
+                wait_vm<(L - 2) * NL < 63 ? (L - 2) * NL : 63>();  // slab phase+1 has landed
+                lds_barrier();                                       // ... for every wave; stage phase free
+                stress_pause<1>(wave, stress_ctr);
+            }
+            if constexpr (LAST && s < FN + 2) p_addr_op(std::integral_constant<int, s>{}, st_next);
+            if constexpr (s >= START) {
+                constexpr int i = s - START;
+                if constexpr (D && i % DS == 0 && i / DS < D) load_op(std::integral_constant<int, D0 + i / DS>{});
+            }
+            if constexpr (LAST) {
+                if constexpr (s >= START && s - START < kPR2B) p_read_b_op(I0{}, std::integral_constant<int, s - START>{});
+                static_for<0, kPR2A>([&](auto i_c) __attribute__((always_inline)) {
+                    if constexpr (p2a_gap(decltype(i_c)::value) == s) p_read_a_op(I0{}, i_c);
+                });
+            } else {
+                if constexpr (s >= START && s - START < kPR1A)
+                    p_read_a_op(std::integral_constant<int, kPA2>{}, std::integral_constant<int, s - START>{});
+                if constexpr (s >= START + kPR1A && s - START - kPR1A < kPR1B)
+                    p_read_b_op(std::integral_constant<int, FN / 2>{}, std::integral_constant<int, s - START - kPR1A>{});
+            }
+            if constexpr (kSplitAdvance ? !LAST : LAST) {
+                static_for<0, kAdvPieces>([&](auto p_c) __attribute__((always_inline)) {
+                    constexpr int p = decltype(p_c)::value;
+                    if constexpr (s == (ADV + p < NSTEP - 1 ? ADV + p : NSTEP - 1)) adv_piece(p_c);
+                });
+            }
+            if constexpr (EPH != 0 && s >= kPEpiGap && (s - kPEpiGap) % 2 == 0) {
+                constexpr int e = (s - kPEpiGap) / 2;  // store e: row block e / (FN/4), t within the half
+                constexpr int t = (EPH == 1 ? 0 : FN / 4) + e % (FN / 4);
+                epi_op(std::integral_constant<int, e / (FN / 4)>{}, std::integral_constant<int, t>{});
+            }
+            if constexpr (D && s + 1 >= START && (s + 1 - START) % DS == 0 && (s + 1 - START) / DS < D)
+                m0_op(std::integral_constant<int, D0 + (s + 1 - START) / DS>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
     // ---- epilogue: cast and store one finished tile, then clear its
     // accumulators for the next (the k == 0 clear).  Conversions are volatile
     // asm so each stays next to its store instead of all being hoisted.  Lanes
@@ -716,7 +876,14 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     stress_pause<3>(wave, stress_ctr);
     wait_vm<(L - 2) * NL + T::DF < 63 ? (L - 2) * NL + T::DF : 63>();
     lds_barrier();
-    read_all(I0{}, I0{}, 0u);
+    if constexpr (PAIR) {
+        // what the first slab's phase 1 expects the previous phase 2 to have read
+        static_for<0, FN + 2>([&](auto q_c) __attribute__((always_inline)) { p_addr_op(q_c, 0u); });
+        static_for<0, kPR2B>([&](auto r_c) __attribute__((always_inline)) { p_read_b_op(I0{}, r_c); });
+        static_for<0, kPR2A>([&](auto i_c) __attribute__((always_inline)) { p_read_a_op(I0{}, i_c); });
+    } else {
+        read_all(I0{}, I0{}, 0u);
+    }
 
     // Each slab's last k-step publishes the next slab and reads its first
     // fragments into the other register set.  Two k-steps per slab: sets 0/1
@@ -725,7 +892,23 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     uint32_t phase = 0;
     bool pend = false;  // a tile's second-half stores are still to go out
     for (sched.init(wid); sched.valid(); sched.next_tile()) {
-        if constexpr (kEpiInterleave) {
+        if constexpr (PAIR) {
+            // one code path per tile (k_blocks >= 2): the first slab's two
+            // phases clear, the last slab's phase 2 stores
+            using I2P = std::integral_constant<int, 2>;
+            using I1P = std::integral_constant<int, 1>;
+            pstep(I1P{}, TRUE_{}, I2P{}, 0u);
+            pstep(I2P{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE);
+            ++phase;
+            for (uint32_t k = 1; k + 1u < k_blocks; ++k, ++phase) {
+                pstep(I1P{}, FALSE_{}, I0{}, 0u);
+                pstep(I2P{}, FALSE_{}, I0{}, ((phase + 1u) % L) * T::STAGE);
+            }
+            pstep(I1P{}, FALSE_{}, I0{}, 0u);
+            epi_state();  // after the previous tile's last stores
+            pstep(I2P{}, FALSE_{}, I1P{}, ((phase + 1u) % L) * T::STAGE);
+            ++phase;
+        } else if constexpr (kEpiInterleave) {
             // rotated: the tile's first k-step, then (last k-step of slab k,
             // first k-step of slab k+1) pairs, then its last k-step; one code
             // path per tile, so the accumulators stay put
@@ -760,13 +943,23 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
     if constexpr (kEpiInterleave) {
         if (pend) {
             gap_nops();  // the last tile's last MFMAs have written their accumulators
-            static_for<kEpiFirst, FM>([&](auto fm_c) __attribute__((always_inline)) {
-                static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
-                    epi_op(fm_c, t_c);
-                    store_gap();
-                    __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PAIR) {
+                static_for<0, FM>([&](auto fm_c) __attribute__((always_inline)) {
+                    static_for<FN / 4, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
+                        epi_op(fm_c, t_c);
+                        store_gap();
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
                 });
-            });
+            } else {
+                static_for<kEpiFirst, FM>([&](auto fm_c) __attribute__((always_inline)) {
+                    static_for<0, FN / 2>([&](auto t_c) __attribute__((always_inline)) {
+                        epi_op(fm_c, t_c);
+                        store_gap();
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                });
+            }
         }
     }
     wait_vm<0>();  // no DMA may still target LDS when the workgroup retires
