@@ -29,7 +29,10 @@
 //   * 256 threads = 4 wavefronts in a 2x2 grid, one per SIMD; every wave
 //     computes a (BM/2) x (BN/2) sub-tile with its accumulators in registers;
 //   * the MFMA is issued with B as its first operand, so a lane's results run
-//     along N and the epilogue writes 16 contiguous bytes per lane.
+//     along N and the epilogue writes 16 contiguous bytes per lane;
+//   * on 256x256x64 tiles each slab's two k-steps reach every accumulator as
+//     two MFMAs in a row (PAIR), the second taking its accumulator input from
+//     the matrix core's forwarding path.
 #pragma once
 
 #include "tile_scheduler.h"
@@ -895,18 +898,16 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         if constexpr (PAIR) {
             // one code path per tile (k_blocks >= 2): the first slab's two
             // phases clear, the last slab's phase 2 stores
-            using I2P = std::integral_constant<int, 2>;
-            using I1P = std::integral_constant<int, 1>;
-            pstep(I1P{}, TRUE_{}, I2P{}, 0u);
-            pstep(I2P{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE);
+            pstep(I1{}, TRUE_{}, I2{}, 0u);
+            pstep(I2{}, TRUE_{}, I0{}, ((phase + 1u) % L) * T::STAGE);
             ++phase;
             for (uint32_t k = 1; k + 1u < k_blocks; ++k, ++phase) {
-                pstep(I1P{}, FALSE_{}, I0{}, 0u);
-                pstep(I2P{}, FALSE_{}, I0{}, ((phase + 1u) % L) * T::STAGE);
+                pstep(I1{}, FALSE_{}, I0{}, 0u);
+                pstep(I2{}, FALSE_{}, I0{}, ((phase + 1u) % L) * T::STAGE);
             }
-            pstep(I1P{}, FALSE_{}, I0{}, 0u);
+            pstep(I1{}, FALSE_{}, I0{}, 0u);
             epi_state();  // after the previous tile's last stores
-            pstep(I2P{}, FALSE_{}, I1P{}, ((phase + 1u) % L) * T::STAGE);
+            pstep(I2{}, FALSE_{}, I1{}, ((phase + 1u) % L) * T::STAGE);
             ++phase;
         } else if constexpr (kEpiInterleave) {
             // rotated: the tile's first k-step, then (last k-step of slab k,
