@@ -45,3 +45,15 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_recorded_traffic_matches_the_kernel_sources():
+    """The HBM traffic the bench line reports comes from profiles/ only while
+    the kernel sources still hash to the value recorded with it; a kernel
+    change without new counter runs would leave `roofline.traffic` null."""
+    t = bench.recorded_traffic("cfg3_8192_bf16")
+    assert t is not None, "profiles/gemm_8192_bf16.md was taken with other kernel sources"
+    assert 402.7e6 <= t < 10 * 402.7e6  # at least the algorithmic bytes of A + B + C
+    t = bench.recorded_traffic("mx_8192_mxfp8", "mx")
+    assert t is not None, "profiles/gemm_8192_mxfp8.md was taken with other kernel sources"
+    assert 272.6e6 <= t < 10 * 272.6e6
