@@ -521,15 +521,15 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int D0 = LAST ? 0 : T::DF;
         // DMA issues are spaced DS MFMAs apart: a burst of them right after the
         // barrier would overflow the texture unit's queue and stall issue
-        constexpr int DS = D ? (AVAIL / D < dma_spacing(BK) ? (AVAIL / D > 0 ? AVAIL / D : 1) : dma_spacing(BK)) : 1;
+        constexpr int DS = D ? (AVAIL / (D ? D : 1) < dma_spacing(BK) ? (AVAIL / (D ? D : 1) > 0 ? AVAIL / (D ? D : 1) : 1) : dma_spacing(BK)) : 1;
         constexpr int QR = SAME ? 0 : R;                   // reads, spread evenly
         constexpr int PER = QR ? (QR + AVAIL - 1) / AVAIL : 0;
         // The loader's step, in the k-step that issues a slab's last DMAs: in
         // the first gap after all of this k-step's memory operations, or in
         // the last gap after its DMA when the operations fill the k-step (the
         // DMAs read the descriptors in place, so none may follow the step).
-        constexpr int MEM_END = START + (D ? (D - 1) * DS + 1 : 0) > START + (PER ? (QR + PER - 1) / PER : 0)
-                                    ? START + (D ? (D - 1) * DS + 1 : 0) : START + (PER ? (QR + PER - 1) / PER : 0);
+        constexpr int MEM_END = START + (D ? (D - 1) * DS + 1 : 0) > START + (PER ? (QR + PER - 1) / (PER ? PER : 1) : 0)
+                                    ? START + (D ? (D - 1) * DS + 1 : 0) : START + (PER ? (QR + PER - 1) / (PER ? PER : 1) : 0);
         constexpr int ADV = MEM_END < NSTEP - 1 ? MEM_END : NSTEP - 1;
         static_for<0, NSTEP>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(64 * 2 * WGN, 1) void tsgemm_kernel(GemmArgs args) 
         constexpr int AVAIL = NSTEP - START - 1;
         constexpr int D = LAST ? T::DF : NL - T::DF;
         constexpr int D0 = LAST ? 0 : T::DF;
-        constexpr int DS = D ? (AVAIL / D < dma_spacing(BK) ? (AVAIL / D > 0 ? AVAIL / D : 1) : dma_spacing(BK)) : 1;
+        constexpr int DS = D ? (AVAIL / (D ? D : 1) < dma_spacing(BK) ? (AVAIL / (D ? D : 1) > 0 ? AVAIL / (D ? D : 1) : 1) : dma_spacing(BK)) : 1;
         constexpr int DMA_END = D ? START + (D - 1) * DS + 1 : 0;
         constexpr int READ_END = LAST ? p2a_gap(kPR2A - 1) + 1 : START + kPR1A + kPR1B;
         constexpr int MEM_END = DMA_END > READ_END ? DMA_END : READ_END;
